@@ -1,0 +1,225 @@
+"""ctypes shim over the plain C fp64 oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and
+the bench's CPU-baseline leg, never by the product path.  It shares no code
+with the GPU library and imports nothing from it.
+
+The functions take and return numpy arrays.  Element types: ``numpy.float16``
+or ``numpy.float32`` inputs (passed to the C code as raw bits with a dtype
+code); planes are ``uint32`` arrays in the packed layout documented in
+``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F16 = 0
+F32 = 1
+
+
+def build() -> str:
+    """Compile oracle.c with gcc into liboracle.so (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared",
+         "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        d = ctypes.c_double
+        L.orc_half_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_half_to_double.restype = d
+        L.orc_double_to_half.argtypes = [d]
+        L.orc_double_to_half.restype = ctypes.c_uint16
+        L.orc_quant_group.argtypes = [P, i, i, P, P, P]
+        L.orc_quant_group.restype = i
+        L.orc_pack.argtypes = [P, i, i, P]
+        L.orc_pack.restype = None
+        L.orc_unpack.argtypes = [P, i, i, P]
+        L.orc_unpack.restype = None
+        L.orc_code_at.argtypes = [P, i, i]
+        L.orc_code_at.restype = i
+        L.orc_quantize_keys.argtypes = [P, i, i, i, i, i, i, i, i, P, P, P]
+        L.orc_quantize_keys.restype = i
+        L.orc_quantize_values.argtypes = [P, i, i, i, i, i, i, i, i, P, P]
+        L.orc_quantize_values.restype = i
+        L.orc_rope.argtypes = [P, i, d, d]
+        L.orc_rope.restype = None
+        L.orc_attend.argtypes = [i, i, i, i, i, i, i, i, i, d, P, P, P, P, P,
+                                 i, P, i, i, i, P]
+        L.orc_attend.restype = i
+        L.orc_attend_dense.argtypes = [i, i, i, i, d, P, P, i, P, i, i, i, P]
+        L.orc_attend_dense.restype = i
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float16:
+        return F16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"oracle inputs are float16 or float32, got {a.dtype}")
+
+
+# ------------------------------------------------------------------ binary16
+
+def half_to_double(bits: int) -> float:
+    return lib().orc_half_to_double(bits)
+
+
+def double_to_half(x: float) -> int:
+    return lib().orc_double_to_half(float(x))
+
+
+# ----------------------------------------------------------------- quantizer
+
+def quant_group(x, bits: int):
+    """Quantize one group. Returns (codes uint8[n], s16 bits, z16 bits)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    codes = np.zeros(x.size, dtype=np.uint8)
+    s = np.zeros(1, dtype=np.uint16)
+    z = np.zeros(1, dtype=np.uint16)
+    rc = lib().orc_quant_group(_ptr(x), x.size, bits, _ptr(codes), _ptr(s), _ptr(z))
+    if rc != 0:
+        raise ValueError("orc_quant_group failed")
+    return codes, int(s[0]), int(z[0])
+
+
+def pack(codes, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    words = np.zeros(codes.size * bits // 32, dtype=np.uint32)
+    lib().orc_pack(_ptr(codes), codes.size, bits, _ptr(words))
+    return words
+
+
+def unpack(words, n: int, bits: int) -> np.ndarray:
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    codes = np.zeros(n, dtype=np.uint8)
+    lib().orc_unpack(_ptr(words), n, bits, _ptr(codes))
+    return codes
+
+
+def plane_shapes(nb, hkv, D, G, kbits, vbits, max_tokens):
+    """Shapes of the packed planes for a cache of capacity max_tokens."""
+    gcap = -(-max_tokens // G)
+    tcap = gcap * G
+    return {
+        "k_codes": (nb, hkv, gcap, D, G * kbits // 32),
+        "k_meta": (nb, hkv, gcap, D),
+        "v_codes": (nb, hkv, tcap, D // G, G * vbits // 32),
+        "v_meta": (nb, hkv, tcap, D // G),
+        "k_tail": (nb, hkv, G, D),
+    }
+
+
+def quantize_keys(k: np.ndarray, bits: int, G: int = 32, max_tokens=None):
+    """Key planes for k[nb][Hkv][T][D]: (k_codes, k_meta, k_tail)."""
+    k = np.ascontiguousarray(k)
+    nb, hkv, T, D = k.shape
+    cap = T if max_tokens is None else max_tokens
+    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1))
+    kc = np.zeros(sh["k_codes"], dtype=np.uint32)
+    km = np.zeros(sh["k_meta"], dtype=np.uint32)
+    kt = np.zeros(sh["k_tail"], dtype=k.dtype)
+    rc = lib().orc_quantize_keys(_ptr(k), _dtype_code(k), nb, hkv, T, D, G,
+                                 bits, sh["k_meta"][2], _ptr(kc), _ptr(km), _ptr(kt))
+    if rc != 0:
+        raise ValueError("orc_quantize_keys failed")
+    return kc, km, kt
+
+
+def quantize_values(v: np.ndarray, bits: int, G: int = 32, max_tokens=None):
+    """Value planes for v[nb][Hkv][T][D]: (v_codes, v_meta)."""
+    v = np.ascontiguousarray(v)
+    nb, hkv, T, D = v.shape
+    cap = T if max_tokens is None else max_tokens
+    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1))
+    vc = np.zeros(sh["v_codes"], dtype=np.uint32)
+    vm = np.zeros(sh["v_meta"], dtype=np.uint32)
+    rc = lib().orc_quantize_values(_ptr(v), _dtype_code(v), nb, hkv, T, D, G,
+                                   bits, sh["v_meta"][2], _ptr(vc), _ptr(vm))
+    if rc != 0:
+        raise ValueError("orc_quantize_values failed")
+    return vc, vm
+
+
+# ---------------------------------------------------------------- attention
+
+def rope(u, p: float, base: float = 10000.0) -> np.ndarray:
+    u = np.array(u, dtype=np.float64)
+    lib().orc_rope(_ptr(u), u.size, float(p), float(base))
+    return u
+
+
+def attend(planes: dict, q: np.ndarray, n: int, kbits: int, vbits: int,
+           hkv: int, G: int = 32, base: float = 10000.0, rows=None) -> np.ndarray:
+    """Decode attention over quantized planes for queries q[nb][Hq][D].
+
+    ``planes`` holds k_codes, k_meta, k_tail, v_codes, v_meta (numpy).  The
+    tail's element type is q's.  ``rows`` = (begin, end) over b*Hq + hq.
+    Returns float64 [rows, D] (all rows: reshaped to [nb, Hq, D])."""
+    q = np.ascontiguousarray(q)
+    nb, hq, D = q.shape
+    kc = np.ascontiguousarray(planes["k_codes"], dtype=np.uint32)
+    km = np.ascontiguousarray(planes["k_meta"], dtype=np.uint32)
+    kt = np.ascontiguousarray(planes["k_tail"]).astype(q.dtype, copy=False)
+    kt = np.ascontiguousarray(kt)
+    vc = np.ascontiguousarray(planes["v_codes"], dtype=np.uint32)
+    vm = np.ascontiguousarray(planes["v_meta"], dtype=np.uint32)
+    gcap = km.shape[2]
+    tcap = vm.shape[2]
+    r0, r1 = (0, nb * hq) if rows is None else rows
+    out = np.zeros((r1 - r0, D), dtype=np.float64)
+    rc = lib().orc_attend(nb, hq, hkv, D, G, kbits, vbits, gcap, tcap, float(base),
+                          _ptr(kc), _ptr(km), _ptr(kt), _ptr(vc), _ptr(vm),
+                          _dtype_code(q), _ptr(q), n, r0, r1, _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_attend failed")
+    if rows is None:
+        return out.reshape(nb, hq, D)
+    return out
+
+
+def attend_dense(k: np.ndarray, v: np.ndarray, q: np.ndarray,
+                 base: float = 10000.0, rows=None) -> np.ndarray:
+    """Full-precision attention over unquantized k, v [nb][Hkv][n][D]."""
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v, dtype=k.dtype)
+    q = np.ascontiguousarray(q, dtype=k.dtype)
+    nb, hkv, n, D = k.shape
+    hq = q.shape[1]
+    r0, r1 = (0, nb * hq) if rows is None else rows
+    out = np.zeros((r1 - r0, D), dtype=np.float64)
+    rc = lib().orc_attend_dense(nb, hq, hkv, D, float(base), _ptr(k), _ptr(v),
+                                _dtype_code(k), _ptr(q), n, r0, r1, _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_attend_dense failed")
+    if rows is None:
+        return out.reshape(nb, hq, D)
+    return out

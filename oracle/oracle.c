@@ -1,0 +1,430 @@
+/*
+ * oracle.c -- plain, slow, single-threaded fp64 reference for KIVI-style
+ * asymmetric KV-cache quantization and the decode attention that reads the
+ * quantized cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the package's smoke check and the bench's
+ * CPU-baseline leg do.  It includes no HIP header and shares no source with
+ * the GPU library.
+ *
+ * Sources (web pages), cited as:
+ *   [GEOM]  "Why KV Cache Geometry Matters More Than Bit Precision for LLM
+ *           Speed" (milik.ai)
+ *   [BITS]  "Your KV Cache Doesn't Have a Bit Problem. It Has a Geometry
+ *           Problem" (Unite.AI article, tastytech.in repost)
+ *   [ROT]   "Rotate, Then Round: The Geometry of KV-Cache Compression"
+ *           (aissential.tech digest)
+ *
+ * What is computed, step by step (every floating-point step in fp64):
+ *   1. Quantize one group of values (uniform asymmetric integer code):
+ *      zero point = group minimum, step = range / (2^B - 1), each element
+ *      rounded to the nearest step.  [BITS, "What Quantization Error Is
+ *      Actually Made Of"]; [GEOM, "Inside the Attention Equation"].
+ *      Readings where the pages are silent: ties go to the even code; the
+ *      zero and the step are stored as IEEE binary16, each rounded once
+ *      (round-to-nearest-even) from the exact value; codes are computed
+ *      against the stored binary16 zero and step; a zero step gives code 0.
+ *   2. Keys are grouped per channel over runs of G consecutive tokens,
+ *      values per token over runs of G consecutive channels.  [BITS, "Keys:
+ *      The Outliers Live in Fixed Channels", "Values: Where the Intuition
+ *      Breaks"]; [GEOM, "Stop Obsessing Over Bits"].
+ *   3. Key tokens that do not yet fill a G-token group stay unquantized in
+ *      a tail buffer.  [BITS, "The Systems Tax, and Why It Is Not a Detail"].
+ *   4. Keys are stored before the rotary position embedding; the rotation is
+ *      applied after dequantization.  [BITS, "Rotary Embeddings Complicate
+ *      the Keys"]; [GEOM, "What Data Scientists Should Do Next"].
+ *      Reading: channels (2i, 2i+1) form a pair (neighbouring channels), the
+ *      pair rotates by p * theta_i with theta_i = base^(-2i/D); the query is
+ *      rotated at position n-1.
+ *   5. Attention output = softmax-weighted sum of the value vectors over all
+ *      cached tokens, scores scaled by 1/sqrt(D).  [BITS, "Values: Where the
+ *      Intuition Breaks"].  Softmax is the plain two-pass form.
+ *
+ * Packed layout (the bit-exact contract shared with the GPU library, which
+ * implements it separately):
+ *   K_CODES u32[nb][Hkv][Gcap][D][Wk]   Wk = G*Bk/32; token j of a group at
+ *                                       bits [j*Bk, j*Bk+Bk) of the group's
+ *                                       little-endian bit string for channel c
+ *   K_META  u32[nb][Hkv][Gcap][D]       binary16 step | binary16 zero << 16
+ *   V_CODES u32[nb][Hkv][Tcap][D/G][Wv] channel j of a channel group at bits
+ *                                       [j*Bv, j*Bv+Bv)
+ *   V_META  u32[nb][Hkv][Tcap][D/G]     binary16 step | binary16 zero << 16
+ *   K_TAIL  dtype[nb][Hkv][G][D]        slot j = token Tq + j, verbatim
+ *
+ * Input element types: ORC_F16 (IEEE binary16 bit patterns) or ORC_F32.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F16 0
+#define ORC_F32 1
+
+/* ---------------------------------------------------------------- binary16 */
+
+/* binary16 -> double, from the IEEE 754 definition of the format. */
+double orc_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);              /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m | 0x400), e - 25); /* (1024+m) * 2^(e-15-10) */
+    return sign ? -v : v;
+}
+
+/* double -> binary16 with one rounding, to nearest, ties to even,
+ * subnormals included, overflow to infinity.  The value is scaled by a power
+ * of two so that one binary16 quantum becomes 1, rounded with nearbyint in the
+ * default (to-nearest-even) mode, and re-encoded. */
+uint16_t orc_double_to_half(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7e00;
+    /* 65504 is the largest finite value; its quantum is 32, so the halfway
+     * point to the next binade is 65520, which rounds to even (infinity). */
+    if (a >= 65520.0)
+        return sign | 0x7c00;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);               /* a = f * 2^e, f in [0.5, 1) */
+    int quantum = (e - 1) - 10; /* exponent of one unit in the last place */
+    if (quantum < -24)
+        quantum = -24;          /* subnormal range: fixed quantum 2^-24 */
+    double r = nearbyint(ldexp(a, -quantum));
+    double v = ldexp(r, quantum); /* the rounded magnitude */
+    if (v == 0.0)
+        return sign;
+    int e2;
+    frexp(v, &e2);
+    int E = e2 - 1; /* v in [2^E, 2^(E+1)) */
+    if (E < -14) {
+        /* subnormal: v = m * 2^-24 */
+        return sign | (uint16_t)ldexp(v, 24);
+    }
+    if (E > 15)
+        return sign | 0x7c00;
+    uint16_t mant = (uint16_t)(ldexp(v, -E) * 1024.0 - 1024.0);
+    return sign | (uint16_t)((E + 15) << 10) | mant;
+}
+
+static double load_elem(const void* p, int dtype, size_t i)
+{
+    if (dtype == ORC_F16)
+        return orc_half_to_double(((const uint16_t*)p)[i]);
+    return (double)((const float*)p)[i];
+}
+
+/* ------------------------------------------------------------ quantizer */
+
+/* Quantize one group of n values with B-bit codes.
+ * [BITS, "What Quantization Error Is Actually Made Of"]: record the smallest
+ * value as the zero point, divide the group's range by 2^B - 1 to get the
+ * step, round every element to the nearest step.
+ * Returns 0, or -1 on bad arguments. */
+int orc_quant_group(const double* x, int n, int bits, uint8_t* codes,
+                    uint16_t* s16_out, uint16_t* z16_out)
+{
+    if (n <= 0 || bits < 1 || bits > 8)
+        return -1;
+    double mn = x[0], mx = x[0];
+    for (int i = 1; i < n; ++i) {
+        if (x[i] < mn) mn = x[i];
+        if (x[i] > mx) mx = x[i];
+    }
+    double levels = (double)((1 << bits) - 1);
+    uint16_t z16 = orc_double_to_half(mn);
+    /* (mx - mn) is exact in fp64 for binary16 and ordinary fp32 inputs; the
+     * fp64 quotient never lands on the wrong side of a binary16 rounding
+     * boundary for such inputs, so this equals one rounding of the exact
+     * quotient. */
+    uint16_t s16 = orc_double_to_half((mx - mn) / levels);
+    double z = orc_half_to_double(z16);
+    double s = orc_half_to_double(s16);
+    int top = (1 << bits) - 1;
+    for (int i = 0; i < n; ++i) {
+        int c = 0;
+        if (s != 0.0) {
+            double r = nearbyint((x[i] - z) / s); /* nearest, ties to even */
+            if (r < 0.0) r = 0.0;
+            if (r > (double)top) r = (double)top;
+            c = (int)r;
+        }
+        codes[i] = (uint8_t)c;
+    }
+    *s16_out = s16;
+    *z16_out = z16;
+    return 0;
+}
+
+/* Pack n codes of `bits` bits, code j at bit offset j*bits of a little-endian
+ * bit string made of 32-bit words.  The word array must hold n*bits/32 words
+ * (n*bits a multiple of 32). */
+void orc_pack(const uint8_t* codes, int n, int bits, uint32_t* words)
+{
+    int nw = n * bits / 32;
+    for (int w = 0; w < nw; ++w)
+        words[w] = 0;
+    for (int j = 0; j < n; ++j) {
+        int bit = j * bits;
+        words[bit / 32] |= (uint32_t)codes[j] << (bit % 32);
+    }
+}
+
+/* Code j of a packed bit string (inverse of orc_pack for one element). */
+int orc_code_at(const uint32_t* words, int j, int bits)
+{
+    int bit = j * bits;
+    return (int)((words[bit / 32] >> (bit % 32)) & ((1u << bits) - 1u));
+}
+
+void orc_unpack(const uint32_t* words, int n, int bits, uint8_t* codes)
+{
+    for (int j = 0; j < n; ++j)
+        codes[j] = (uint8_t)orc_code_at(words, j, bits);
+}
+
+/* Key planes for T cached tokens: groups g < T/G are quantized per channel
+ * (group = one channel over tokens gG .. gG+G-1); tokens from Tq = (T/G)*G
+ * on are copied verbatim into the tail.  Planes sized for gcap groups. */
+int orc_quantize_keys(const void* k, int dtype, int nb, int hkv, int T, int D,
+                      int G, int bits, int gcap, uint32_t* k_codes,
+                      uint32_t* k_meta, void* k_tail)
+{
+    if (G <= 0 || (G * bits) % 32 != 0 || T < 0 || T / G > gcap)
+        return -1;
+    int wk = G * bits / 32;
+    int ngroups = T / G;
+    int tq = ngroups * G;
+    size_t esz = (dtype == ORC_F16) ? 2 : 4;
+    double* x = (double*)malloc(sizeof(double) * (size_t)G);
+    uint8_t* codes = (uint8_t*)malloc((size_t)G);
+    if (!x || !codes) {
+        free(x);
+        free(codes);
+        return -2;
+    }
+    for (int b = 0; b < nb; ++b)
+        for (int h = 0; h < hkv; ++h) {
+            size_t bh = (size_t)b * hkv + h;
+            for (int g = 0; g < ngroups; ++g)
+                for (int c = 0; c < D; ++c) {
+                    for (int j = 0; j < G; ++j)
+                        x[j] = load_elem(k, dtype,
+                                         (bh * T + (size_t)g * G + j) * D + c);
+                    uint16_t s16, z16;
+                    orc_quant_group(x, G, bits, codes, &s16, &z16);
+                    size_t gc = (bh * gcap + g) * D + c;
+                    orc_pack(codes, G, bits, k_codes + gc * wk);
+                    k_meta[gc] = (uint32_t)s16 | ((uint32_t)z16 << 16);
+                }
+            for (int t = tq; t < T; ++t)
+                memcpy((char*)k_tail + ((bh * G + (t - tq)) * D) * esz,
+                       (const char*)k + ((bh * T + t) * D) * esz, esz * D);
+        }
+    free(x);
+    free(codes);
+    return 0;
+}
+
+/* Value planes for T tokens: every token is quantized at once, per channel
+ * group (group = channels cg*G .. cg*G+G-1 of one token). */
+int orc_quantize_values(const void* v, int dtype, int nb, int hkv, int T,
+                        int D, int G, int bits, int tcap, uint32_t* v_codes,
+                        uint32_t* v_meta)
+{
+    if (G <= 0 || D % G != 0 || (G * bits) % 32 != 0 || T < 0 || T > tcap)
+        return -1;
+    int wv = G * bits / 32;
+    int ncg = D / G;
+    double* x = (double*)malloc(sizeof(double) * (size_t)G);
+    uint8_t* codes = (uint8_t*)malloc((size_t)G);
+    if (!x || !codes) {
+        free(x);
+        free(codes);
+        return -2;
+    }
+    for (int b = 0; b < nb; ++b)
+        for (int h = 0; h < hkv; ++h) {
+            size_t bh = (size_t)b * hkv + h;
+            for (int t = 0; t < T; ++t)
+                for (int cg = 0; cg < ncg; ++cg) {
+                    for (int j = 0; j < G; ++j)
+                        x[j] = load_elem(v, dtype,
+                                         (bh * T + t) * D + (size_t)cg * G + j);
+                    uint16_t s16, z16;
+                    orc_quant_group(x, G, bits, codes, &s16, &z16);
+                    size_t tc = (bh * tcap + t) * ncg + cg;
+                    orc_pack(codes, G, bits, v_codes + tc * wv);
+                    v_meta[tc] = (uint32_t)s16 | ((uint32_t)z16 << 16);
+                }
+        }
+    free(x);
+    free(codes);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ RoPE */
+
+/* Rotate vector u (length D, D even) in place to position p: the channel
+ * pair (2i, 2i+1) turns by the angle p * base^(-2i/D).
+ * [BITS, "Rotary Embeddings Complicate the Keys"]. */
+void orc_rope(double* u, int D, double p, double base)
+{
+    for (int i = 0; i < D / 2; ++i) {
+        double theta = pow(base, -2.0 * i / (double)D);
+        double a = p * theta;
+        double c = cos(a), s = sin(a);
+        double u0 = u[2 * i], u1 = u[2 * i + 1];
+        u[2 * i] = u0 * c - u1 * s;
+        u[2 * i + 1] = u0 * s + u1 * c;
+    }
+}
+
+/* ------------------------------------------------------------- attention */
+
+static double dequant(uint32_t meta, int code)
+{
+    double s = orc_half_to_double((uint16_t)(meta & 0xffff));
+    double z = orc_half_to_double((uint16_t)(meta >> 16));
+    return z + s * (double)code;
+}
+
+/* Softmax-weighted sum over n tokens given their scores and a callback-free
+ * value table (n x D doubles).  Two-pass softmax. */
+static void softmax_sum(const double* score, const double* vals, int n, int D,
+                        double* out)
+{
+    double m = score[0];
+    for (int t = 1; t < n; ++t)
+        if (score[t] > m) m = score[t];
+    double l = 0.0;
+    for (int c = 0; c < D; ++c)
+        out[c] = 0.0;
+    for (int t = 0; t < n; ++t) {
+        double w = exp(score[t] - m);
+        l += w;
+        for (int c = 0; c < D; ++c)
+            out[c] += w * vals[(size_t)t * D + c];
+    }
+    for (int c = 0; c < D; ++c)
+        out[c] /= l;
+}
+
+/* Decode attention over the quantized cache of n tokens (the planes above),
+ * for the output rows r in [row_begin, row_end), r = b*Hq + hq.  Query head
+ * hq reads KV head hq / (Hq/Hkv).  out holds (row_end-row_begin) x D doubles.
+ *   keys t < Tq: dequantize per channel group, then rotate to position t;
+ *   keys t >= Tq: tail slot t - Tq, rotated to position t;
+ *   query: rotated to position n-1;
+ *   score_t = q'.k'_t / sqrt(D); out = sum_t softmax(score)_t * vhat_t. */
+int orc_attend(int nb, int hq, int hkv, int D, int G, int kbits, int vbits,
+               int gcap, int tcap, double base, const uint32_t* k_codes,
+               const uint32_t* k_meta, const void* k_tail,
+               const uint32_t* v_codes, const uint32_t* v_meta, int dtype,
+               const void* q, int n, int row_begin, int row_end, double* out)
+{
+    if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 || D % G != 0 ||
+        n > tcap || n / G > gcap || row_begin < 0 || row_end > nb * hq)
+        return -1;
+    int wk = G * kbits / 32, wv = G * vbits / 32, ncg = D / G;
+    int tq = (n / G) * G;
+    double* score = (double*)malloc(sizeof(double) * (size_t)n);
+    double* vals = (double*)malloc(sizeof(double) * (size_t)n * D);
+    double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)D);
+    uint8_t* codes = (uint8_t*)malloc((size_t)G);
+    if (!score || !vals || !qr || !kr || !codes) {
+        free(score); free(vals); free(qr); free(kr); free(codes);
+        return -2;
+    }
+    int group = hq / hkv;
+    for (int r = row_begin; r < row_end; ++r) {
+        int b = r / hq, h = r % hq, kvh = h / group;
+        size_t bh = (size_t)b * hkv + kvh;
+        for (int c = 0; c < D; ++c)
+            qr[c] = load_elem(q, dtype, (size_t)r * D + c);
+        orc_rope(qr, D, (double)(n - 1), base);
+        for (int t = 0; t < n; ++t) {
+            if (t < tq) {
+                int g = t / G, j = t % G;
+                for (int c = 0; c < D; ++c) {
+                    size_t gc = (bh * gcap + g) * D + c;
+                    kr[c] = dequant(k_meta[gc],
+                                    orc_code_at(k_codes + gc * wk, j, kbits));
+                }
+            } else {
+                for (int c = 0; c < D; ++c)
+                    kr[c] = load_elem(k_tail, dtype,
+                                      (bh * G + (t - tq)) * D + c);
+            }
+            orc_rope(kr, D, (double)t, base);
+            double dot = 0.0;
+            for (int c = 0; c < D; ++c)
+                dot += qr[c] * kr[c];
+            score[t] = dot / sqrt((double)D);
+            for (int cg = 0; cg < ncg; ++cg) {
+                size_t tc = (bh * tcap + t) * ncg + cg;
+                orc_unpack(v_codes + tc * wv, G, vbits, codes);
+                for (int j = 0; j < G; ++j)
+                    vals[(size_t)t * D + cg * G + j] =
+                        dequant(v_meta[tc], codes[j]);
+            }
+        }
+        softmax_sum(score, vals, n, D, out + (size_t)(r - row_begin) * D);
+    }
+    free(score); free(vals); free(qr); free(kr); free(codes);
+    return 0;
+}
+
+/* The same attention over unquantized keys and values k, v laid out
+ * [nb][Hkv][n][D] (the full-precision reference a quantized cache should
+ * approach as the bit width grows). */
+int orc_attend_dense(int nb, int hq, int hkv, int D, double base,
+                     const void* k, const void* v, int dtype, const void* q,
+                     int n, int row_begin, int row_end, double* out)
+{
+    if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 || row_begin < 0 ||
+        row_end > nb * hq)
+        return -1;
+    double* score = (double*)malloc(sizeof(double) * (size_t)n);
+    double* vals = (double*)malloc(sizeof(double) * (size_t)n * D);
+    double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!score || !vals || !qr || !kr) {
+        free(score); free(vals); free(qr); free(kr);
+        return -2;
+    }
+    int group = hq / hkv;
+    for (int r = row_begin; r < row_end; ++r) {
+        int b = r / hq, h = r % hq, kvh = h / group;
+        size_t bh = (size_t)b * hkv + kvh;
+        for (int c = 0; c < D; ++c)
+            qr[c] = load_elem(q, dtype, (size_t)r * D + c);
+        orc_rope(qr, D, (double)(n - 1), base);
+        for (int t = 0; t < n; ++t) {
+            for (int c = 0; c < D; ++c) {
+                kr[c] = load_elem(k, dtype, (bh * n + t) * D + c);
+                vals[(size_t)t * D + c] = load_elem(v, dtype, (bh * n + t) * D + c);
+            }
+            orc_rope(kr, D, (double)t, base);
+            double dot = 0.0;
+            for (int c = 0; c < D; ++c)
+                dot += qr[c] * kr[c];
+            score[t] = dot / sqrt((double)D);
+        }
+        softmax_sum(score, vals, n, D, out + (size_t)(r - row_begin) * D);
+    }
+    free(score); free(vals); free(qr); free(kr);
+    return 0;
+}
