@@ -1,0 +1,179 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) library for a KIVI-style asymmetric
+ * quantized KV cache and the decode attention that reads it.
+ *
+ * The method (from the web pages this library implements):
+ *   - uniform asymmetric integer quantization of a group: zero point = the
+ *     group's minimum, step = range / (2^B - 1), every element rounded to the
+ *     nearest step ("Your KV Cache Doesn't Have a Bit Problem. It Has a
+ *     Geometry Problem", section "What Quantization Error Is Actually Made
+ *     Of");
+ *   - keys grouped per channel over runs of G consecutive tokens, values per
+ *     token over runs of G consecutive channels (same page, sections "Keys:
+ *     The Outliers Live in Fixed Channels" and "Values: Where the Intuition
+ *     Breaks"; "Why KV Cache Geometry Matters More Than Bit Precision for
+ *     LLM Speed", section "Stop Obsessing Over Bits");
+ *   - key tokens that do not yet fill a group wait unquantized in a tail
+ *     buffer and are quantized as a group once G have accumulated; values
+ *     are quantized as each token arrives ("...Bit Problem...", section "The
+ *     Systems Tax, and Why It Is Not a Detail");
+ *   - keys are quantized before the rotary position embedding, which is
+ *     applied after dequantization inside attention ("...Bit Problem...",
+ *     section "Rotary Embeddings Complicate the Keys");
+ *   - decode attention reads the whole cache for every generated token
+ *     ("...Bit Problem...", section "Why the KV Cache Is Where This Bites").
+ *
+ * Conventions shared by every entry point
+ *   - All pointers named d_* are device (HIP) pointers; everything else is
+ *     host memory.  The caller owns every buffer, including the workspace;
+ *     the library never allocates or frees device memory.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call except kvq_create only enqueues work on that stream and returns;
+ *     results are valid once the caller has synchronized it.  Calls on one
+ *     handle must be ordered on one stream by the caller.  A handle is not
+ *     thread-safe.
+ *   - Every function returns KVQ_OK (0) or a negative KVQ_ERR_* code.  All
+ *     argument and state checks run before anything is enqueued: on error the
+ *     handle's state is unchanged and no GPU work was queued.
+ *   - Element types (kvq_config.dtype): KVQ_F16 (IEEE binary16) or KVQ_F32.
+ *     Keys, values, queries and the key tail use that type; the output is
+ *     always fp32.  Non-finite inputs are undefined behaviour.
+ *   - Supported: group == 32; key_bits, value_bits in {2, 4, 8};
+ *     head_dim in {64, 128}; q_heads a multiple of kv_heads with
+ *     q_heads / kv_heads in {1, 2, 4, 8}.
+ *
+ * Packed planes inside the workspace (byte offsets from kvq_get_layout; each
+ * plane 256-byte aligned).  Gcap = ceil(max_tokens / G), Tcap = Gcap * G,
+ * Wk = G * key_bits / 32, Wv = G * value_bits / 32 (32-bit words per group):
+ *   K_CODES u32[batch][kv_heads][Gcap][head_dim][Wk]
+ *           code of token j of key group g, channel c, at bits
+ *           [j*key_bits, j*key_bits + key_bits) of the Wk-word little-endian
+ *           bit string (word j*key_bits/32, LSB first)
+ *   K_META  u32[batch][kv_heads][Gcap][head_dim]
+ *           binary16 step in bits 0..15, binary16 zero point in bits 16..31
+ *   V_CODES u32[batch][kv_heads][Tcap][head_dim/G][Wv]
+ *           code of channel cg*G + j of token t at bits [j*value_bits, ...)
+ *   V_META  u32[batch][kv_heads][Tcap][head_dim/G]   (as K_META)
+ *   K_TAIL  dtype[batch][kv_heads][G][head_dim]
+ *           slot j holds key token Tq + j verbatim, Tq = floor(n/G)*G
+ * The step and zero are each rounded once, to nearest-even, from the exact
+ * value (range/(2^B-1) and the minimum); the code of x is the integer nearest
+ * to (x - zero)/step computed exactly, ties to even, clamped to
+ * [0, 2^B - 1]; a zero step gives code 0.
+ *
+ * Rotary embedding: channels (2i, 2i+1) form a pair rotated by the angle
+ * p * rope_base^(-2i/head_dim); key token t at position t, the query at
+ * position n-1 (n = cached tokens, the newest token included).  Scores are
+ * scaled by 1/sqrt(head_dim); query head h reads KV head
+ * h / (q_heads / kv_heads).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KVQ_OK = 0,
+    KVQ_ERR_ARG = -1,         /* null pointer, bad dimension, bad value     */
+    KVQ_ERR_UNSUPPORTED = -2, /* valid but not built: bits, G, head_dim ... */
+    KVQ_ERR_WORKSPACE = -3,   /* workspace too small or not 256-B aligned   */
+    KVQ_ERR_STATE = -4,       /* prefill on a non-empty cache, attend on an
+                                 empty one                                  */
+    KVQ_ERR_CAPACITY = -5,    /* the call would exceed max_tokens           */
+    KVQ_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+};
+
+enum { KVQ_F16 = 0, KVQ_F32 = 1 };
+
+typedef struct kvq_config {
+    int32_t batch;      /* sequences, >= 1                                  */
+    int32_t q_heads;    /* query heads, multiple of kv_heads                */
+    int32_t kv_heads;   /* key/value heads, >= 1                            */
+    int32_t head_dim;   /* D: 64 or 128                                     */
+    int32_t max_tokens; /* per-sequence capacity, >= 1                      */
+    int32_t group;      /* G: must be 32                                    */
+    int32_t key_bits;   /* 2, 4 or 8                                        */
+    int32_t value_bits; /* 2, 4 or 8                                        */
+    int32_t dtype;      /* KVQ_F16 or KVQ_F32                               */
+    float rope_base;    /* > 1, e.g. 10000                                  */
+} kvq_config;
+
+typedef struct kvq_layout {
+    size_t k_codes, k_meta, v_codes, v_meta, k_tail; /* byte offsets        */
+    size_t rope_group, rope_offset, partials, counters;
+    size_t total_bytes;   /* == kvq_workspace_bytes(cfg)                     */
+    int32_t gcap, tcap;   /* Gcap and Tcap above                             */
+    int32_t max_splits;   /* token splits per (sequence, KV head) at most    */
+} kvq_layout;
+
+typedef struct kvq kvq_t; /* opaque; lives in host memory */
+
+/* Bytes of device workspace a cache with this configuration needs (pure
+ * host; 0 if the configuration is invalid or unsupported). */
+size_t kvq_workspace_bytes(const kvq_config* cfg);
+
+/* Create a cache handle over a caller-owned device workspace d_ws of
+ * ws_bytes bytes (>= kvq_workspace_bytes, 256-byte aligned).  Writes the
+ * rotary tables into the workspace with a blocking copy on the null stream
+ * (the only blocking call) and sets the cached length n to 0.  The
+ * workspace contents are otherwise not initialised.  *out receives the
+ * handle (host memory, freed by kvq_destroy).
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
+int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes,
+               kvq_t** out);
+
+/* Quantize a whole prompt of n_tokens tokens into the empty cache.
+ * d_k, d_v: dtype[batch][kv_heads][n_tokens][head_dim], keys before the
+ * rotary embedding.  Key groups g < n_tokens/G are quantized per channel
+ * (K_CODES, K_META); the last n_tokens mod G keys go to K_TAIL; every value
+ * token is quantized per channel group (V_CODES, V_META).  Sets n = n_tokens.
+ * n_tokens == 0 is allowed and enqueues nothing.
+ * Errors: KVQ_ERR_ARG (null handle or pointers with n_tokens > 0, negative
+ * n_tokens), KVQ_ERR_STATE (n != 0), KVQ_ERR_CAPACITY (n_tokens >
+ * max_tokens), KVQ_ERR_HIP. */
+int kvq_quantize_prefill(kvq_t* h, const void* d_k, const void* d_v,
+                         int32_t n_tokens, void* stream);
+
+/* Append one token per sequence: d_k, d_v are dtype[batch][kv_heads]
+ * [head_dim].  The value is quantized at once; the key goes to tail slot
+ * n mod G, and when that fills the tail (n+1 a multiple of G) the G tail
+ * keys are quantized as key group n/G in the same launch.  Sets n = n + 1.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_CAPACITY (n == max_tokens), KVQ_ERR_HIP. */
+int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v,
+                     void* stream);
+
+/* Decode attention of one query per head over all n cached tokens.
+ * d_q: dtype[batch][q_heads][head_dim], before the rotary embedding.
+ * d_out: float[batch][q_heads][head_dim].  Uses the workspace's partials
+ * and counters regions as scratch, so two attend calls on one handle must
+ * not run concurrently.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (n == 0), KVQ_ERR_HIP. */
+int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream);
+
+/* Free the handle (host memory only; the workspace is untouched).
+ * Errors: KVQ_ERR_ARG (null). */
+int kvq_destroy(kvq_t* h);
+
+/* Cached tokens n (pure host; -1 for a null handle). */
+int32_t kvq_length(const kvq_t* h);
+
+/* Plane offsets inside the workspace (pure host).  Errors: KVQ_ERR_ARG. */
+int kvq_get_layout(const kvq_t* h, kvq_layout* out);
+
+/* Workspace layout for a configuration without a handle (pure host).
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED. */
+int kvq_layout_for(const kvq_config* cfg, kvq_layout* out);
+
+/* Static description of a status code (pure host). */
+const char* kvq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

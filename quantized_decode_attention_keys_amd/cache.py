@@ -1,0 +1,124 @@
+"""``QuantizedKVCache``: a thin object over the C ABI.  PyTorch supplies the
+device workspace, the input/output tensors and the stream; every step of the
+computation runs in the library's HIP kernels."""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+_DTYPES = {torch.float16: L.KVQ_F16, torch.float32: L.KVQ_F32}
+
+
+def _check(status: int, what: str):
+    if status != L.KVQ_OK:
+        raise L.KvqError(status, what)
+
+
+class QuantizedKVCache:
+    """One layer's quantized KV cache for `batch` sequences.
+
+    k/v inputs are [batch][kv_heads][T][head_dim] (prefill) or
+    [batch][kv_heads][head_dim] (append), q is [batch][q_heads][head_dim], all
+    contiguous tensors of `dtype` on the cache's device; keys and queries are
+    before the rotary embedding.  Calls enqueue on the current torch stream
+    (or `stream`) and return at once."""
+
+    def __init__(self, batch, q_heads, kv_heads, head_dim, max_tokens, key_bits=2,
+                 value_bits=2, dtype=torch.float16, rope_base=10000.0, group=32,
+                 device=None):
+        if dtype not in _DTYPES:
+            raise TypeError("dtype must be torch.float16 or torch.float32")
+        self.cfg = L.KvqConfig(batch, q_heads, kv_heads, head_dim, max_tokens, group,
+                               key_bits, value_bits, _DTYPES[dtype], rope_base)
+        self.dtype = dtype
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        st, self.layout = L.kvq_layout_for(self.cfg)
+        _check(st, "kvq_layout_for")
+        nbytes = self.layout.total_bytes
+        # torch's caching allocator returns 512-byte aligned blocks
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        st, self.handle = L.kvq_create(self.cfg, self.workspace.data_ptr(), nbytes)
+        _check(st, "kvq_create")
+
+    # ------------------------------------------------------------ helpers
+    def _stream(self, stream):
+        s = torch.cuda.current_stream(self.device) if stream is None else stream
+        return s.cuda_stream
+
+    def _arg(self, t, shape, name):
+        if not isinstance(t, torch.Tensor) or t.dtype != self.dtype or t.device != self.device \
+                or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: expected a contiguous {self.dtype} tensor of shape "
+                             f"{tuple(shape)} on {self.device}, got "
+                             f"{getattr(t, 'dtype', None)} {tuple(getattr(t, 'shape', ()))}")
+        return t.data_ptr()
+
+    # --------------------------------------------------------------- API
+    def __len__(self):
+        return L.kvq_length(self.handle)
+
+    def prefill(self, k, v, stream=None):
+        c = self.cfg
+        n = k.shape[2] if k.dim() == 4 else -1
+        shape = (c.batch, c.kv_heads, n, c.head_dim)
+        pk = self._arg(k, shape, "k")
+        pv = self._arg(v, shape, "v")
+        _check(L.kvq_quantize_prefill(self.handle, pk, pv, n, self._stream(stream)),
+               "kvq_quantize_prefill")
+
+    def append(self, k, v, stream=None):
+        c = self.cfg
+        shape = (c.batch, c.kv_heads, c.head_dim)
+        pk = self._arg(k, shape, "k")
+        pv = self._arg(v, shape, "v")
+        _check(L.kvq_append_token(self.handle, pk, pv, self._stream(stream)),
+               "kvq_append_token")
+
+    def attend(self, q, out=None, stream=None):
+        c = self.cfg
+        pq = self._arg(q, (c.batch, c.q_heads, c.head_dim), "q")
+        if out is None:
+            out = torch.empty((c.batch, c.q_heads, c.head_dim), dtype=torch.float32,
+                              device=self.device)
+        elif out.dtype != torch.float32 or not out.is_contiguous() or \
+                tuple(out.shape) != (c.batch, c.q_heads, c.head_dim):
+            raise ValueError("out must be a contiguous float32 [batch][q_heads][head_dim] tensor")
+        _check(L.kvq_attend_decode(self.handle, pq, out.data_ptr(), self._stream(stream)),
+               "kvq_attend_decode")
+        return out
+
+    def planes(self):
+        """Views of the packed planes inside the workspace (no copy)."""
+        c, lay = self.cfg, self.layout
+        G = c.group
+        nb, h, D = c.batch, c.kv_heads, c.head_dim
+        wk, wv = G * c.key_bits // 32, G * c.value_bits // 32
+        ws = self.workspace
+
+        def view(off, shape, dt):
+            n = 1
+            for s in shape:
+                n *= s
+            esz = torch.tensor([], dtype=dt).element_size()
+            return ws[off:off + n * esz].view(dt).view(shape)
+
+        return {
+            "k_codes": view(lay.k_codes, (nb, h, lay.gcap, D, wk), torch.int32),
+            "k_meta": view(lay.k_meta, (nb, h, lay.gcap, D), torch.int32),
+            "v_codes": view(lay.v_codes, (nb, h, lay.tcap, D // G, wv), torch.int32),
+            "v_meta": view(lay.v_meta, (nb, h, lay.tcap, D // G), torch.int32),
+            "k_tail": view(lay.k_tail, (nb, h, G, D), self.dtype),
+        }
+
+    def close(self):
+        if getattr(self, "handle", None):
+            L.kvq_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

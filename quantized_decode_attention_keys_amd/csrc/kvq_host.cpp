@@ -1,0 +1,256 @@
+// kvq_host.cpp -- the C ABI declared in include/kvq.h: configuration checks,
+// workspace layout, the host-side length counter, rotary tables and kernel
+// dispatch.  Every check runs before anything is enqueued.
+#include "kvq.h"
+#include "kvq_internal.h"
+
+#include <cmath>
+#include <cstdlib>
+#include <new>
+#include <vector>
+
+struct kvq {
+    kvq_config cfg;
+    kvq_layout layout;
+    char* ws;
+    int32_t n;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetBlocks = 1024;  // attend blocks wanted per launch
+constexpr int kMaxSplits = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_config(const kvq_config* c)
+{
+    if (!c)
+        return KVQ_ERR_ARG;
+    if (c->batch < 1 || c->q_heads < 1 || c->kv_heads < 1 || c->head_dim < 1 ||
+        c->max_tokens < 1 || c->group < 1 || c->key_bits < 1 || c->value_bits < 1 ||
+        !(c->rope_base > 1.0f) || !std::isfinite(c->rope_base) || c->q_heads % c->kv_heads != 0 ||
+        (c->dtype != KVQ_F16 && c->dtype != KVQ_F32))
+        return KVQ_ERR_ARG;
+    const int qpk = c->q_heads / c->kv_heads;
+    if (c->group != kvqi::kGroup || (c->head_dim != 64 && c->head_dim != 128) ||
+        (c->key_bits != 2 && c->key_bits != 4 && c->key_bits != 8) ||
+        (c->value_bits != 2 && c->value_bits != 4 && c->value_bits != 8) ||
+        (qpk != 1 && qpk != 2 && qpk != 4 && qpk != 8))
+        return KVQ_ERR_UNSUPPORTED;
+    // keep every plane index inside 2^31 elements per (sequence, head) and
+    // the grid dimensions inside their limits
+    if ((long long)c->max_tokens > (1LL << 26) || (long long)c->batch * c->q_heads > (1LL << 24) ||
+        (long long)c->batch * c->kv_heads > 65535)
+        return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
+void make_layout(const kvq_config* c, kvq_layout* L)
+{
+    const size_t nb = c->batch, hkv = c->kv_heads, hq = c->q_heads, D = c->head_dim;
+    const size_t G = c->group;
+    const int gcap = (c->max_tokens + c->group - 1) / c->group;
+    const size_t tcap = (size_t)gcap * G;
+    const size_t wk = G * c->key_bits / 32, wv = G * c->value_bits / 32;
+    const size_t esz = c->dtype == KVQ_F16 ? 2 : 4;
+    int ms = (kTargetBlocks + (int)(nb * hkv) - 1) / (int)(nb * hkv);
+    if (ms > kMaxSplits) ms = kMaxSplits;
+    if (ms > gcap + 1) ms = gcap + 1;
+    if (ms < 1) ms = 1;
+    size_t off = 0;
+    L->k_codes = off;   off = align_up(off + nb * hkv * gcap * D * wk * 4);
+    L->k_meta = off;    off = align_up(off + nb * hkv * gcap * D * 4);
+    L->v_codes = off;   off = align_up(off + nb * hkv * tcap * (D / G) * wv * 4);
+    L->v_meta = off;    off = align_up(off + nb * hkv * tcap * (D / G) * 4);
+    L->k_tail = off;    off = align_up(off + nb * hkv * G * D * esz);
+    L->rope_group = off; off = align_up(off + (size_t)gcap * (D / 2) * 8);
+    L->rope_offset = off; off = align_up(off + G * (D / 2) * 8);
+    L->partials = off;  off = align_up(off + nb * hq * (size_t)ms * (D + 2) * 4);
+    L->counters = off;  off = align_up(off + nb * hq * 4);
+    L->total_bytes = off;
+    L->gcap = gcap;
+    L->tcap = (int32_t)tcap;
+    L->max_splits = ms;
+}
+
+kvqi::Planes planes_of(const kvq* h)
+{
+    const kvq_layout& L = h->layout;
+    kvqi::Planes p;
+    p.k_codes = reinterpret_cast<uint32_t*>(h->ws + L.k_codes);
+    p.k_meta = reinterpret_cast<uint32_t*>(h->ws + L.k_meta);
+    p.v_codes = reinterpret_cast<uint32_t*>(h->ws + L.v_codes);
+    p.v_meta = reinterpret_cast<uint32_t*>(h->ws + L.v_meta);
+    p.k_tail = h->ws + L.k_tail;
+    p.rope_group = reinterpret_cast<const float2*>(h->ws + L.rope_group);
+    p.rope_offset = reinterpret_cast<const float2*>(h->ws + L.rope_offset);
+    p.partials = reinterpret_cast<float*>(h->ws + L.partials);
+    p.counters = reinterpret_cast<uint32_t*>(h->ws + L.counters);
+    p.nb = h->cfg.batch;
+    p.hq = h->cfg.q_heads;
+    p.hkv = h->cfg.kv_heads;
+    p.D = h->cfg.head_dim;
+    p.kbits = h->cfg.key_bits;
+    p.vbits = h->cfg.value_bits;
+    p.gcap = L.gcap;
+    p.tcap = L.tcap;
+    p.max_splits = L.max_splits;
+    p.dtype = h->cfg.dtype;
+    return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_workspace_bytes(const kvq_config* cfg)
+{
+    if (check_config(cfg) != KVQ_OK)
+        return 0;
+    kvq_layout L;
+    make_layout(cfg, &L);
+    return L.total_bytes;
+}
+
+int kvq_layout_for(const kvq_config* cfg, kvq_layout* out)
+{
+    if (!out)
+        return KVQ_ERR_ARG;
+    const int st = check_config(cfg);
+    if (st != KVQ_OK)
+        return st;
+    make_layout(cfg, out);
+    return KVQ_OK;
+}
+
+int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes, kvq_t** out)
+{
+    if (!out || !d_ws)
+        return KVQ_ERR_ARG;
+    const int st = check_config(cfg);
+    if (st != KVQ_OK)
+        return st;
+    kvq_layout L;
+    make_layout(cfg, &L);
+    if (ws_bytes < L.total_bytes || (reinterpret_cast<uintptr_t>(d_ws) % kAlign) != 0)
+        return KVQ_ERR_WORKSPACE;
+    // Rotary tables, computed in fp64 and stored as fp32 (cos, sin):
+    //   group table  [g][i] = angle g*G*theta_i,  offset table [j][i] = j*theta_i,
+    // theta_i = base^(-2i/D); position p = g*G + j composes as a product.
+    const int D = cfg->head_dim, NP = D / 2, G = cfg->group;
+    std::vector<float> grp((size_t)L.gcap * NP * 2), offs((size_t)G * NP * 2);
+    for (int i = 0; i < NP; ++i) {
+        const double theta = std::pow((double)cfg->rope_base, -2.0 * i / (double)D);
+        for (int g = 0; g < L.gcap; ++g) {
+            const double a = (double)g * G * theta;
+            grp[((size_t)g * NP + i) * 2] = (float)std::cos(a);
+            grp[((size_t)g * NP + i) * 2 + 1] = (float)std::sin(a);
+        }
+        for (int j = 0; j < G; ++j) {
+            const double a = (double)j * theta;
+            offs[((size_t)j * NP + i) * 2] = (float)std::cos(a);
+            offs[((size_t)j * NP + i) * 2 + 1] = (float)std::sin(a);
+        }
+    }
+    char* ws = static_cast<char*>(d_ws);
+    if (hipMemcpy(ws + L.rope_group, grp.data(), grp.size() * sizeof(float),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(ws + L.rope_offset, offs.data(), offs.size() * sizeof(float),
+                  hipMemcpyHostToDevice) != hipSuccess)
+        return KVQ_ERR_HIP;
+    kvq* h = new (std::nothrow) kvq;
+    if (!h)
+        return KVQ_ERR_ARG;
+    h->cfg = *cfg;
+    h->layout = L;
+    h->ws = ws;
+    h->n = 0;
+    *out = h;
+    return KVQ_OK;
+}
+
+int kvq_quantize_prefill(kvq_t* h, const void* d_k, const void* d_v, int32_t n_tokens,
+                         void* stream)
+{
+    if (!h || n_tokens < 0)
+        return KVQ_ERR_ARG;
+    if (n_tokens > 0 && (!d_k || !d_v))
+        return KVQ_ERR_ARG;
+    if (h->n != 0)
+        return KVQ_ERR_STATE;
+    if (n_tokens > h->cfg.max_tokens)
+        return KVQ_ERR_CAPACITY;
+    if (n_tokens == 0)
+        return KVQ_OK;
+    const int st = hip_status(kvqi::launch_quantize_prefill(
+        planes_of(h), d_k, d_v, n_tokens, static_cast<hipStream_t>(stream)));
+    if (st == KVQ_OK)
+        h->n = n_tokens;
+    return st;
+}
+
+int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v, void* stream)
+{
+    if (!h || !d_k || !d_v)
+        return KVQ_ERR_ARG;
+    if (h->n >= h->cfg.max_tokens)
+        return KVQ_ERR_CAPACITY;
+    const int st = hip_status(
+        kvqi::launch_append(planes_of(h), d_k, d_v, h->n, static_cast<hipStream_t>(stream)));
+    if (st == KVQ_OK)
+        h->n += 1;
+    return st;
+}
+
+int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream)
+{
+    if (!h || !d_q || !d_out)
+        return KVQ_ERR_ARG;
+    if (h->n == 0)
+        return KVQ_ERR_STATE;
+    const int n = h->n;
+    const int units = n / h->cfg.group + (n % h->cfg.group ? 1 : 0);
+    int splits = h->layout.max_splits;
+    if (splits > units)
+        splits = units;
+    return hip_status(kvqi::launch_attend(planes_of(h), d_q, d_out, n, splits,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int kvq_destroy(kvq_t* h)
+{
+    if (!h)
+        return KVQ_ERR_ARG;
+    delete h;
+    return KVQ_OK;
+}
+
+int32_t kvq_length(const kvq_t* h) { return h ? h->n : -1; }
+
+int kvq_get_layout(const kvq_t* h, kvq_layout* out)
+{
+    if (!h || !out)
+        return KVQ_ERR_ARG;
+    *out = h->layout;
+    return KVQ_OK;
+}
+
+const char* kvq_strerror(int status)
+{
+    switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case KVQ_ERR_STATE: return "call not valid in the cache's current state";
+    case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// kvq_internal.h -- declarations shared by the host API (kvq_host.cpp) and
+// the gfx950 kernels (kvq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvqi {
+
+constexpr int kGroup = 32;  // G: tokens per key group, channels per value group
+
+// Everything a kernel needs to address the planes of one cache.
+struct Planes {
+    uint32_t* k_codes;   // [nb][hkv][gcap][D][wk]
+    uint32_t* k_meta;    // [nb][hkv][gcap][D]
+    uint32_t* v_codes;   // [nb][hkv][tcap][D/G][wv]
+    uint32_t* v_meta;    // [nb][hkv][tcap][D/G]
+    void* k_tail;        // dtype[nb][hkv][G][D]
+    const float2* rope_group;   // [gcap][D/2]  (cos, sin) of g*G*theta_i
+    const float2* rope_offset;  // [G][D/2]     (cos, sin) of j*theta_i
+    float* partials;     // [nb*hq][max_splits][D+2]
+    uint32_t* counters;  // [nb*hq]
+    int nb, hq, hkv, D, kbits, vbits, gcap, tcap, max_splits, dtype;
+};
+
+// Launch wrappers (kvq_kernels.hip).  All enqueue on `stream` and return the
+// hipGetLastError() status of the launches.
+hipError_t launch_quantize_prefill(const Planes& p, const void* k, const void* v,
+                                   int n_tokens, hipStream_t stream);
+hipError_t launch_append(const Planes& p, const void* k, const void* v, int n,
+                         hipStream_t stream);
+hipError_t launch_attend(const Planes& p, const void* q, float* out, int n,
+                         int splits, hipStream_t stream);
+
+}  // namespace kvqi

@@ -1,0 +1,73 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI on
+seeded synthetic inputs and compare it with the oracle on the same bytes."""
+import numpy as np
+import torch
+
+import oracle
+import synth
+from quantized_decode_attention_keys_amd import QuantizedKVCache
+
+TOL = 2e-3  # attention: max|out - ref| <= TOL * max|ref| over the output tensor
+
+_TORCH = {np.dtype(np.float16): torch.float16, np.dtype(np.float32): torch.float32}
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def to_gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def make_cache(cfg, max_tokens):
+    return QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
+                            cfg.key_bits, cfg.value_bits, _TORCH[cfg.np_dtype],
+                            rope_base=cfg.rope_base, device=dev())
+
+
+def gpu_planes(cache):
+    torch.cuda.synchronize()
+    out = {}
+    for k, t in cache.planes().items():
+        a = t.cpu().numpy()
+        out[k] = a.view(np.uint32) if a.dtype == np.int32 else a
+    return out
+
+
+def oracle_planes(cfg, k, v, max_tokens):
+    kc, km, kt = oracle.quantize_keys(k, cfg.key_bits, cfg.group, max_tokens=max_tokens)
+    vc, vm = oracle.quantize_values(v, cfg.value_bits, cfg.group, max_tokens=max_tokens)
+    return dict(k_codes=kc, k_meta=km, k_tail=kt, v_codes=vc, v_meta=vm)
+
+
+def assert_planes_equal(gp, op, n, G=32, seqs=None):
+    """Bit-exact comparison of every slot that holds data at length n."""
+    ng, tq = n // G, (n // G) * G
+    sel = slice(None) if seqs is None else list(seqs)
+    g = {k: a[sel] for k, a in gp.items()}
+    for name, lim in (("k_codes", ng), ("k_meta", ng), ("v_codes", n), ("v_meta", n)):
+        a, b = g[name][:, :, :lim], op[name][:, :, :lim]
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)
+            raise AssertionError(f"{name}: {len(bad)} mismatches, first at {bad[0].tolist()}: "
+                                 f"gpu {a[tuple(bad[0])]:#x} oracle {b[tuple(bad[0])]:#x}")
+    at, bt = g["k_tail"][:, :, :n - tq], op["k_tail"][:, :, :n - tq]
+    assert np.array_equal(at.view(np.uint8), bt.view(np.uint8)), "k_tail differs"
+
+
+def assert_attention_close(out, ref, tol=TOL):
+    err = np.abs(out - ref).max()
+    scale = np.abs(ref).max()
+    assert err <= tol * scale, f"attention max err {err:.3e} > {tol} * {scale:.3e}"
+    return err / scale
+
+
+def run_prefill(cfg, n, max_tokens=None, seed=0):
+    """Prefill n tokens on the GPU; return (cache, k, v) with host inputs."""
+    max_tokens = max(n, 1) if max_tokens is None else max_tokens
+    k = synth.make_keys(cfg, seed, 0, n)
+    v = synth.make_values(cfg, seed, 0, n)
+    cache = make_cache(cfg, max_tokens)
+    cache.prefill(to_gpu(k), to_gpu(v))
+    return cache, k, v

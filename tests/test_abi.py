@@ -1,0 +1,109 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every function
+include/kvq.h declares, computes layouts, and rejects bad arguments before
+any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_decode_attention_keys_amd as kvq
+from quantized_decode_attention_keys_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def cfg(**kw):
+    base = dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, max_tokens=1000, group=32,
+                key_bits=2, value_bits=4, dtype=L.KVQ_F16, rope_base=10000.0)
+    base.update(kw)
+    return L.KvqConfig(**base)
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert "kvq_attend_decode" in names and len(names) >= 10
+    syms = subprocess.check_output(["nm", "-D", "--defined-only", L.library_path()]).decode()
+    exported = set(re.findall(r" T (\w+)", syms))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L.lib(), n)
+
+
+def test_python_binding_names_match_the_header():
+    for n in _declared():
+        assert callable(getattr(kvq, n)), n
+
+
+def test_layout_sizes_alignment_and_order():
+    c = cfg()
+    st, lay = L.kvq_layout_for(c)
+    assert st == L.KVQ_OK
+    assert lay.gcap == 32 and lay.tcap == 1024
+    offs = [lay.k_codes, lay.k_meta, lay.v_codes, lay.v_meta, lay.k_tail, lay.rope_group,
+            lay.rope_offset, lay.partials, lay.counters, lay.total_bytes]
+    assert offs == sorted(offs)
+    assert all(o % 256 == 0 for o in offs)
+    nb, h, D = 2, 2, 128
+    assert lay.k_meta - lay.k_codes >= nb * h * 32 * D * 2 * 4       # Wk = 2
+    assert lay.v_codes - lay.k_meta >= nb * h * 32 * D * 4
+    assert lay.v_meta - lay.v_codes >= nb * h * 1024 * 4 * 4 * 4     # D/G = 4, Wv = 4
+    assert lay.k_tail - lay.v_meta >= nb * h * 1024 * 4 * 4
+    assert lay.rope_group - lay.k_tail >= nb * h * 32 * D * 2
+    assert L.kvq_workspace_bytes(c) == lay.total_bytes
+    assert lay.max_splits >= 1
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, L.KVQ_ERR_ARG),
+    ("q_heads", 3, L.KVQ_ERR_ARG),           # not a multiple of kv_heads
+    ("head_dim", 96, L.KVQ_ERR_UNSUPPORTED),
+    ("group", 64, L.KVQ_ERR_UNSUPPORTED),
+    ("key_bits", 3, L.KVQ_ERR_UNSUPPORTED),
+    ("value_bits", 16, L.KVQ_ERR_UNSUPPORTED),
+    ("q_heads", 32, L.KVQ_ERR_UNSUPPORTED),  # 16 query heads per KV head
+    ("dtype", 7, L.KVQ_ERR_ARG),
+    ("rope_base", 0.5, L.KVQ_ERR_ARG),
+    ("max_tokens", 0, L.KVQ_ERR_ARG),
+])
+def test_bad_configs_rejected_on_host(field, value, status):
+    c = cfg(**{field: value})
+    assert L.kvq_workspace_bytes(c) == 0
+    st, _ = L.kvq_layout_for(c)
+    assert st == status
+    # create fails the same way before touching the device
+    st, h = L.kvq_create(c, 0x10000, 1 << 40)
+    assert st == status and h is None
+
+
+def test_create_rejects_bad_workspace_before_any_hip_call():
+    c = cfg()
+    need = L.kvq_workspace_bytes(c)
+    assert L.kvq_create(c, 0, need)[0] == L.KVQ_ERR_ARG
+    assert L.kvq_create(c, 0x10000, need - 1)[0] == L.KVQ_ERR_WORKSPACE
+    assert L.kvq_create(c, 0x10080, need)[0] == L.KVQ_ERR_WORKSPACE   # not 256-B aligned
+    assert L.lib().kvq_create(None, ctypes.c_void_p(0x10000), need, None) == L.KVQ_ERR_ARG
+
+
+def test_null_handle_calls():
+    assert L.kvq_length(None) == -1
+    assert L.kvq_destroy(None) == L.KVQ_ERR_ARG
+    assert L.kvq_get_layout(None)[0] == L.KVQ_ERR_ARG
+    assert L.kvq_quantize_prefill(None, 1, 1, 4, None) == L.KVQ_ERR_ARG
+    assert L.kvq_append_token(None, 1, 1, None) == L.KVQ_ERR_ARG
+    assert L.kvq_attend_decode(None, 1, 1, None) == L.KVQ_ERR_ARG
+
+
+def test_strerror_covers_every_status():
+    for s in (L.KVQ_OK, L.KVQ_ERR_ARG, L.KVQ_ERR_UNSUPPORTED, L.KVQ_ERR_WORKSPACE,
+              L.KVQ_ERR_STATE, L.KVQ_ERR_CAPACITY, L.KVQ_ERR_HIP):
+        assert L.kvq_strerror(s) != "unknown status"
+    assert L.kvq_strerror(12345) == "unknown status"

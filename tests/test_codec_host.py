@@ -1,0 +1,75 @@
+"""CPU parity of the GPU library's exact arithmetic (binary16 rounding and
+the code of each element, kvq_codec.h compiled for the host) against the
+oracle and numpy.  The kernels run the same source on the device."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "quantized_decode_attention_keys_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    out = tmp_path_factory.mktemp("shim") / "libcodecshim.so"
+    subprocess.check_call(
+        ["/opt/rocm/bin/hipcc", "-O2", "-fPIC", "-shared", "--offload-arch=gfx950",
+         "-I", CSRC, os.path.join(ROOT, "tests", "codec_host_shim.cpp"), "-o", str(out)],
+        stderr=subprocess.DEVNULL)
+    L = ctypes.CDLL(str(out))
+    L.shim_double_to_half.argtypes = [ctypes.c_double]
+    L.shim_double_to_half.restype = ctypes.c_uint32
+    L.shim_half_to_double.argtypes = [ctypes.c_uint32]
+    L.shim_half_to_double.restype = ctypes.c_double
+    L.shim_quant_group.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.shim_quant_group.restype = ctypes.c_uint32
+    return L
+
+
+def test_half_conversions_exhaustive(shim, orc):
+    for b in range(0x7C00):
+        for s in (0, 0x8000):
+            h = b | s
+            assert shim.shim_half_to_double(h) == orc.half_to_double(h)
+            a = orc.half_to_double(b)
+            nb = orc.half_to_double(b + 1) if b + 1 < 0x7C00 else 65536.0
+            m = (a + nb) / 2
+            for x in (a, m, np.nextafter(m, -1e9), np.nextafter(m, 1e9)):
+                xs = -x if s else x
+                assert shim.shim_double_to_half(xs) == orc.double_to_half(xs), (hex(h), xs)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_group_codes_match_oracle(shim, orc, bits, dt):
+    rng = np.random.default_rng(bits)
+    groups = []
+    for _ in range(3000):
+        x = rng.standard_normal(32) * 10.0 ** rng.uniform(-4, 3)
+        if rng.random() < 0.3:
+            x[rng.integers(32)] *= 50
+        with np.errstate(over="ignore"):
+            x = x.astype(dt)
+        # non-finite inputs and zero/step outside the binary16 range are
+        # undefined behaviour of the format
+        rng16 = (float(x.max()) - float(x.min())) / (2 ** bits - 1)
+        if np.all(np.isfinite(x)) and np.abs(x).max() < 65504 and rng16 < 65504:
+            groups.append(x)
+    # exact ties: values half-way between levels of a binary16 grid
+    for _ in range(500):
+        s = 2.0 ** rng.integers(-8, 3)
+        z = float(np.float16(rng.integers(-64, 64) * s))
+        top = 2 ** bits - 1
+        x = np.concatenate([[z, z + top * s], z + (rng.integers(0, top, 30) + 0.5) * s])
+        groups.append(x.astype(dt))
+    groups.append(np.full(32, 1.25, dtype=dt))
+    for x in groups:
+        xf = np.ascontiguousarray(x.astype(np.float32))
+        codes = np.zeros(32, dtype=np.uint8)
+        meta = shim.shim_quant_group(xf.ctypes.data, 32, bits, codes.ctypes.data)
+        oc, s16, z16 = orc.quant_group(x.astype(np.float64), bits)
+        assert meta == (s16 | (z16 << 16))
+        assert np.array_equal(codes, oc)
