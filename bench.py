@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Decode-attention throughput of the quantized KV cache on one MI355X.
+
+One step = one decode step for the whole batch of one layer: append the new
+token (key into the full-precision tail, flushed into a quantized group when
+G keys have accumulated; value quantized at once), then decode attention of
+one query per head over every cached token (unpack, dequantize, rotary
+embedding, q.k, online softmax, weighted sum of values).
+
+The timed steps rotate over R independent caches (R chosen so that R caches
+exceed twice the 256 MB Infinity Cache), so a cache is never still resident
+in that cache when its step starts: the bytes come from HBM.
+
+Prints one JSON line.  value = decode-attention algorithmic bytes moved per
+second over the timed steps (wall clock, launches included); the roofline
+object reports the attention kernel alone, timed with HIP events on the
+stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
+INFINITY_CACHE = 256 << 20  # bytes
+
+
+def attend_bytes(cfg, n: int) -> int:
+    """Algorithmic bytes of one decode-attention call at length n: packed key
+    codes + key meta + key tail + value codes + value meta + q + out."""
+    G, D = cfg.group, cfg.head_dim
+    nbh = cfg.batch * cfg.kv_heads
+    esz = 2 if cfg.dtype == "float16" else 4
+    tq = n // G * G
+    return (nbh * tq * D * cfg.key_bits // 8 + nbh * (tq // G) * D * 4
+            + nbh * (n - tq) * D * esz
+            + nbh * n * D * cfg.value_bits // 8 + nbh * n * (D // G) * 4
+            + cfg.batch * cfg.q_heads * D * esz + cfg.batch * cfg.q_heads * D * 4)
+
+
+def prefill_bytes(cfg, n: int) -> int:
+    """Quantize-and-pack of n tokens: K and V read once, planes written."""
+    G, D = cfg.group, cfg.head_dim
+    nbh = cfg.batch * cfg.kv_heads
+    esz = 2 if cfg.dtype == "float16" else 4
+    tq = n // G * G
+    return (2 * nbh * n * D * esz
+            + nbh * tq * D * cfg.key_bits // 8 + nbh * (tq // G) * D * 4
+            + nbh * (n - tq) * D * esz
+            + nbh * n * D * cfg.value_bits // 8 + nbh * n * (D // G) * 4)
+
+
+def cpu_baseline(cfg, n: int, budget_s: float = 12.0):
+    """The oracle (plain single-threaded fp64 C) on a bounded sample of the
+    same workload: decode attention for whole sequences, rows timed until
+    about budget_s seconds of CPU work."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    q = synth.make_query(cfg, 0, 0)
+    rows_done, t_total, bytes_done = 0, 0.0, 0
+    one = synth.scaled(cfg, batch=1)
+    per_row = attend_bytes(one, n) / cfg.q_heads
+    for b in range(cfg.batch):
+        k = synth.make_keys(cfg, 0, 0, n, seqs=[b])
+        v = synth.make_values(cfg, 0, 0, n, seqs=[b])
+        kc, km, kt = oracle.quantize_keys(k, cfg.key_bits, cfg.group)
+        vc, vm = oracle.quantize_values(v, cfg.value_bits, cfg.group)
+        pl = dict(k_codes=kc, k_meta=km, k_tail=kt, v_codes=vc, v_meta=vm)
+        for r in range(cfg.q_heads):
+            t0 = time.perf_counter()
+            oracle.attend(pl, q[b:b + 1], n, cfg.key_bits, cfg.value_bits, cfg.kv_heads,
+                          cfg.group, cfg.rope_base, rows=(r, r + 1))
+            t_total += time.perf_counter() - t0
+            rows_done += 1
+            bytes_done += per_row
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(bytes_done / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"decode attention of {rows_done} of {cfg.batch * cfg.q_heads} (sequence, head) "
+                  f"rows at n={n}, {t_total:.1f} s on one host core "
+                  f"(host has {os.cpu_count()} cores); same algorithmic bytes per row as the GPU",
+        "tokens_per_s": round(rows_done / cfg.q_heads / t_total, 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="llama2_7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--caches", type=int, default=0, help="rotating caches (0 = auto)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU component in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_decode_attention_keys_amd import QuantizedKVCache
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = synth.CONFIGS[args.config]
+    n = cfg.n_tokens
+    tdt = torch.float16 if cfg.dtype == "float16" else torch.float32
+    total_steps = args.warmup + args.steps
+
+    cache_bytes = attend_bytes(cfg, n)
+    R = args.caches or max(2, math.ceil(2 * INFINITY_CACHE / cache_bytes) + 1)
+    visits = math.ceil(total_steps / R)
+    max_tokens = n + visits
+
+    # inputs: a prompt of n-1 tokens, then one new token per visit
+    k = torch.from_numpy(synth.make_keys(cfg, 0, 0, n - 1)).to(dev)
+    v = torch.from_numpy(synth.make_values(cfg, 0, 0, n - 1)).to(dev)
+    k_new = torch.from_numpy(synth.make_keys(cfg, 0, n - 1, n - 1 + visits)).to(dev)
+    v_new = torch.from_numpy(synth.make_values(cfg, 0, n - 1, n - 1 + visits)).to(dev)
+    k_new = [k_new[:, :, i].contiguous() for i in range(visits)]
+    v_new = [v_new[:, :, i].contiguous() for i in range(visits)]
+    q = torch.from_numpy(synth.make_query(cfg, 0, 0)).to(dev)
+    out = torch.empty((cfg.batch, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+
+    caches = [QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
+                               cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev)
+              for _ in range(R)]
+    # prefill (quantize-and-pack of the whole prompt), timed per cache
+    pf_ms = []
+    for c in caches:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        c.prefill(k, v)
+        e1.record()
+        torch.cuda.synchronize()
+        pf_ms.append(e0.elapsed_time(e1))
+    del k, v
+    torch.cuda.synchronize()
+
+    # The timed loop calls the C ABI directly with precomputed device
+    # pointers so that host overhead stays below GPU time per step and the
+    # GPU queue never runs dry (then the events time the kernels themselves).
+    from quantized_decode_attention_keys_amd import _lib as L
+    lib = L.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    handles = [c.handle for c in caches]
+    kp = [t.data_ptr() for t in k_new]
+    vp = [t.data_ptr() for t in v_new]
+    qp, op = q.data_ptr(), out.data_ptr()
+    append, attend = lib.kvq_append_token, lib.kvq_attend_decode
+
+    def step(s, ev=None):
+        h = handles[s % R]
+        i = s // R
+        st = append(h, kp[i], vp[i], stream)
+        if ev is not None:
+            ev[0].record()
+        st |= attend(h, qp, op, stream)
+        if ev is not None:
+            ev[1].record()
+        return st
+
+    status = 0
+    for s in range(args.warmup):
+        status |= step(s)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    lengths = [n - 1 + (args.warmup + j) // R + 1 for j in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        status |= step(args.warmup + j, evs[j])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if status != 0:
+        raise RuntimeError(f"a library call failed during the timed steps (status bits {status})")
+    if [len(c) for c in caches] != [n - 1 + len(range(r, total_steps, R)) for r in range(R)]:
+        raise RuntimeError("cache lengths do not match the steps issued")
+
+    wall = t1 - t0
+    total_bytes = sum(attend_bytes(cfg, L) for L in lengths)
+    value = total_bytes / wall / 1e9
+    attend_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    att_avg_s = float(attend_ms.mean()) / 1e3
+    bytes_per_launch = total_bytes / len(lengths)
+    achieved = bytes_per_launch / att_avg_s / 1e9
+
+    res = {
+        "metric": "quantized decode-attention effective KV GB/s (% of HBM peak); tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "batch": cfg.batch, "q_heads": cfg.q_heads, "kv_heads": cfg.kv_heads,
+            "head_dim": cfg.head_dim, "context": n, "key_bits": cfg.key_bits,
+            "value_bits": cfg.value_bits, "group": cfg.group, "kv_dtype": cfg.dtype,
+            "context_during_steps": [min(lengths), max(lengths)],
+            "rotating_caches": R,
+            "parallelism": "single GPU",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(cfg.batch * args.steps / wall, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "decode attention, HIP events around each kvq_attend_decode call in the timed loop",
+            "bytes_per_launch": int(bytes_per_launch),
+            "avg_launch_us": round(att_avg_s * 1e6, 3),
+            "p10_p90_us": [round(float(np.percentile(attend_ms, 10)) * 1e3, 3),
+                           round(float(np.percentile(attend_ms, 90)) * 1e3, 3)],
+        },
+        "prefill": {
+            "tokens": n - 1,
+            "median_ms": round(float(np.median(pf_ms)), 4),
+            "GB_per_s": round(prefill_bytes(cfg, n - 1) / (np.median(pf_ms) / 1e3) / 1e9, 2),
+            "tokens_per_s": round(cfg.batch * (n - 1) / (np.median(pf_ms) / 1e3), 1),
+        },
+    }
+    for c in caches:
+        c.close()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, n)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

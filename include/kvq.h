@@ -105,7 +105,7 @@ typedef struct kvq_config {
 
 typedef struct kvq_layout {
     size_t k_codes, k_meta, v_codes, v_meta, k_tail; /* byte offsets        */
-    size_t rope_group, rope_offset, partials, counters;
+    size_t rope_group, rope_offset, partials;
     size_t total_bytes;   /* == kvq_workspace_bytes(cfg)                     */
     int32_t gcap, tcap;   /* Gcap and Tcap above                             */
     int32_t max_splits;   /* token splits per (sequence, KV head) at most    */
@@ -150,8 +150,8 @@ int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v,
 /* Decode attention of one query per head over all n cached tokens.
  * d_q: dtype[batch][q_heads][head_dim], before the rotary embedding.
  * d_out: float[batch][q_heads][head_dim].  Uses the workspace's partials
- * and counters regions as scratch, so two attend calls on one handle must
- * not run concurrently.
+ * region as scratch, so two attend calls on one handle must not run
+ * concurrently.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (n == 0), KVQ_ERR_HIP. */
 int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream);
 

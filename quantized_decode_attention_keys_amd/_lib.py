@@ -59,7 +59,6 @@ class KvqLayout(ctypes.Structure):
         ("rope_group", ctypes.c_size_t),
         ("rope_offset", ctypes.c_size_t),
         ("partials", ctypes.c_size_t),
-        ("counters", ctypes.c_size_t),
         ("total_bytes", ctypes.c_size_t),
         ("gcap", ctypes.c_int32),
         ("tcap", ctypes.c_int32),

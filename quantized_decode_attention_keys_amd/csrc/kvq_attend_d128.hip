@@ -1,0 +1,12 @@
+// kvq_attend_d128.hip -- decode-attention kernels instantiated for head_dim 128.
+#include "kvq_attend_kernel.h"
+
+namespace kvqi {
+
+hipError_t launch_attend_d128(const Planes& p, const void* q, float* out, int n, int splits,
+                             int waves, hipStream_t stream)
+{
+    return launch_attend_d<128>(p, q, out, n, splits, waves, stream);
+}
+
+}  // namespace kvqi

@@ -1,0 +1,12 @@
+// kvq_attend_d64.hip -- decode-attention kernels instantiated for head_dim 64.
+#include "kvq_attend_kernel.h"
+
+namespace kvqi {
+
+hipError_t launch_attend_d64(const Planes& p, const void* q, float* out, int n, int splits,
+                             int waves, hipStream_t stream)
+{
+    return launch_attend_d<64>(p, q, out, n, splits, waves, stream);
+}
+
+}  // namespace kvqi

@@ -1,0 +1,576 @@
+// kvq_attend_kernel.h -- fused decode attention over the quantized cache for
+// gfx950: unpack -> dequantize -> rotary embedding -> q.k -> online softmax
+// -> weighted sum of values.  When the token range of a (sequence, KV head)
+// is split over several blocks, a small second kernel merges their partials.
+//
+// Method (web pages): keys are stored per channel over G-token groups and
+// rotated after dequantization ("Your KV Cache Doesn't Have a Bit
+// Problem...", sections "Keys: The Outliers Live in Fixed Channels" and
+// "Rotary Embeddings Complicate the Keys"); the output is the softmax-weighted
+// sum of the per-token-quantized value vectors (section "Values: Where the
+// Intuition Breaks"); the whole cache is read for every generated token
+// (section "Why the KV Cache Is Where This Bites").
+//
+// Work decomposition.  Grid = (splits, batch * kv_heads), W waves per block
+// (W from the launch).  Each wave takes whole key groups in turn (waves never
+// wait on each other inside the loop), keeps its own online-softmax state,
+// and prefetches the next group's key and value words while it computes the
+// current one.  The block merges its waves at the end; with one split it
+// writes the output, otherwise (o, m, l) partials for the combine kernel.
+//
+// Key side, one group of 32 tokens: lane = channel pair i (64 pairs for
+// head_dim 128; for head_dim 64 a wave takes two groups, 32 lanes each).
+// Writing q' for the rotated query and (x, y) = (z0 + s0 c0, z1 + s1 c1) for
+// the dequantized pair of token t = gG + j, the pair's score term is
+//   Re[ conj(q'_i) e^{i t theta_i} (x + i y) ]
+//     = Re[ T_j (Q_g (x + i y)) ],  T_j = e^{i j theta_i},  Q_g = conj(q'_i) e^{i gG theta_i},
+// so per (group, pair) six constants fold dequantization and the group
+// rotation, and per token the lane spends 4 FMAs on Q_g (x + i y) and 2 on
+// the per-token twiddle T_j, which stays in registers for the whole kernel.
+// The 32 per-pair partial scores are summed across lanes through LDS.
+//
+// Code unpacking.  A B-bit field masked in place inside a 16-bit half of a
+// code word, with its lowest bit at position e <= 9, is the binary16 bit
+// pattern of the subnormal c * 2^(e-24): exact, and read directly as an fp16
+// operand by v_fma_mix_f32.  Fields that would reach the exponent bits are
+// first shifted down.  The power of two 2^(e-24) is folded into the
+// per-token twiddle (keys) or into one rescale at the end (values), so a
+// 32-bit word of codes costs one AND per two codes plus one shift.
+//
+// Value side: lane = one 32-bit code word of a token row (32/B channels) x a
+// token slot; the per-token weight p_t * step multiplies the codes and
+// p_t * zero is accumulated once per (token, channel group).
+#pragma once
+
+#include "kvq_internal.h"
+
+#include <hip/hip_fp16.h>
+
+namespace kvqi {
+namespace {
+
+constexpr int G = kGroup;
+constexpr float kLog2e = 1.4426950408889634f;
+// Block size limit: 12 waves (up to 168 VGPRs per lane) with one query head
+// per KV head, 8 waves (up to 256 VGPRs) when several query heads share one.
+constexpr int kMaxWaves = 12;
+template <int QPK>
+constexpr int max_waves() { return QPK == 1 ? 12 : 8; }
+
+__device__ __forceinline__ float h2f(uint32_t bits16)
+{
+    return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xffffu)));
+}
+
+// Element idx of an fp16 (dtype 0) or fp32 (dtype 1) array.
+__device__ __forceinline__ float ldf(const void* base, size_t idx, int dtype)
+{
+    return dtype == 0 ? __half2float(static_cast<const __half*>(base)[idx])
+                      : static_cast<const float*>(base)[idx];
+}
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b)
+{
+    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+// N consecutive 32-bit words (N a multiple of 4, 16-byte aligned address).
+template <int N>
+__device__ __forceinline__ void load_words(const uint32_t* __restrict__ src, uint32_t (&w)[N])
+{
+    static_assert(N % 4 == 0, "vector loads of 4 words");
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+        const uint4 v = reinterpret_cast<const uint4*>(src)[k];
+        w[4 * k] = v.x;
+        w[4 * k + 1] = v.y;
+        w[4 * k + 2] = v.z;
+        w[4 * k + 3] = v.w;
+    }
+}
+
+// Layout of B-bit codes inside one 32-bit word: the low 16-bit half holds
+// fields 0..TPH-1, the high half the next TPH; field f of a half sits at bits
+// [f*B, f*B + B).  Fields f < DIRECT lie inside the fp16 mantissa (bits
+// 0..9) and are masked in place; the others are read after a right shift by
+// SHIFT bits.
+template <int B>
+struct Codec {
+    static constexpr int TPH = 16 / B;        // fields per 16-bit half
+    static constexpr int DIRECT = 10 / B;     // fields readable in place
+    static constexpr int SHIFT = DIRECT * B;
+    static constexpr uint32_t M2 = ((1u << B) - 1u) | (((1u << B) - 1u) << 16);
+    // bit position of field f (as read) inside its half
+    static constexpr int pos(int f) { return f < DIRECT ? f * B : (f - DIRECT) * B; }
+    // distinct positions: 0, B, ..., (DIRECT-1)*B
+    static constexpr int NSCALE = DIRECT;
+    // field f of both halves, masked, as a pair of binary16 subnormals
+    __device__ static __forceinline__ uint32_t field(uint32_t w, uint32_t w_shifted, int f)
+    {
+        return (f < DIRECT ? w : w_shifted) & (M2 << pos(f));
+    }
+};
+
+__device__ __forceinline__ float lo_h(uint32_t v) { return __half2float(__ushort_as_half((unsigned short)(v & 0xffffu))); }
+__device__ __forceinline__ float hi_h(uint32_t v) { return __half2float(__ushort_as_half((unsigned short)(v >> 16))); }
+
+// Value of v in another lane of the same 16-lane row (DPP, VALU only).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane k <-> 7-k within each 8
+constexpr int kDppMirror = 0x140;     // lane k <-> 15-k within each 16
+
+// Maximum over the wave: four DPP steps inside each 16-lane row, then two
+// cross-row exchanges.
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+template <int D, int KB, int VB, int QPK>
+struct Shape {
+    static constexpr int NP = D / 2;           // channel pairs
+    static constexpr int GPW = 64 / NP;        // key groups per wave step
+    static constexpr int TPW = G * GPW;        // tokens per wave step
+    static constexpr int WK = KB;              // words per (key group, channel)
+    static constexpr int WV = VB;              // words per (token, value group)
+    static constexpr int NCG = D / G;          // value groups per token
+    static constexpr int WPT = NCG * WV;       // value code words per token
+    static constexpr int TS = 64 / WPT;        // token slots in the value phase
+    static constexpr int VTOK = TPW / TS;      // value tokens per lane per step
+    static constexpr int NC = 32 / VB;         // channels per value word
+    static constexpr int RED_STRIDE = 33;      // floats per lane row of the reduce buffer
+    static_assert(64 % WPT == 0 && TPW % TS == 0, "value lane mapping");
+};
+
+// Everything one wave step reads from memory, loaded one step ahead.
+template <int WK, int VTOK>
+struct StepData {
+    uint32_t kw[2 * WK];   // key codes of the lane's two channels
+    uint2 km;              // their (step, zero) meta words
+    float2 rg;             // e^{i g G theta_i}
+    uint32_t vw[VTOK];     // value code word per value token
+    uint32_t vm[VTOK];     // value meta word per value token
+};
+
+// Per-wave online-softmax state and value accumulators.
+template <int QPK, int NC>
+struct WaveState {
+    float m[QPK];      // running max (base-2 logits), uniform across the wave
+    float l[QPK];      // this lane's share of the running sum
+    float z[QPK];      // sum_t p_t * zero_{t, group of this lane's word}
+    float o[QPK][NC];  // sum_t p_t * step * code * 2^(pos-24) per channel of the word
+};
+
+// Plane pointers of one (sequence, KV head); every index below them fits in
+// 32 bits (the host caps max_tokens), so loads use a scalar base plus a
+// 32-bit lane offset.
+struct HeadPlanes {
+    const uint32_t* kc;   // [gcap][D][WK]
+    const uint32_t* km;   // [gcap][D]
+    const uint32_t* vc;   // [tcap][WPT]
+    const uint32_t* vm;   // [tcap][NCG]
+};
+
+template <int D, int KB, int VB, int QPK>
+__device__ __forceinline__ void load_step(const HeadPlanes& hp, const float2* __restrict__ rope_group,
+                                          int lane, int gb, int g1,
+                                          StepData<KB, Shape<D, KB, VB, QPK>::VTOK>& sd)
+{
+    using S = Shape<D, KB, VB, QPK>;
+    const unsigned i = lane % S::NP, gsub = lane / S::NP;
+    const unsigned g = (unsigned)min(gb + (int)gsub, g1 - 1);  // clamped: always a real group
+    const unsigned gc = g * D + 2 * i;
+    load_words<2 * S::WK>(hp.kc + gc * S::WK, sd.kw);
+    sd.km = *reinterpret_cast<const uint2*>(hp.km + gc);
+    sd.rg = rope_group[g * S::NP + i];
+    const unsigned vw = lane % S::WPT, vslot = lane / S::WPT, vcg = vw / S::WV;
+    const int t_last = g1 * G - 1;
+#pragma unroll
+    for (int k = 0; k < S::VTOK; ++k) {
+        const unsigned t = (unsigned)min(gb * G + (int)vslot + k * S::TS, t_last);
+        sd.vw[k] = hp.vc[t * S::WPT + vw];
+        sd.vm[k] = hp.vm[t * S::NCG + vcg];
+    }
+}
+
+// Softmax update for one wave step and accumulation of its value tokens.
+// Lane `lane` holds score s[h] of token tt = lane (head_dim 64) or lane & 31
+// (head_dim 128), i.e. token t_base + tt; tokens at or past t_end are absent
+// (their value words may be anything: their weight is exactly 0).
+template <int D, int KB, int VB, int QPK>
+__device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
+                                               const float (&s)[QPK], const uint32_t* vwords,
+                                               const uint32_t* vmetas,
+                                               WaveState<QPK, 32 / VB>& st)
+{
+    using S = Shape<D, KB, VB, QPK>;
+    using C = Codec<VB>;
+    const int tt_own = (S::NP == 64) ? (lane & 31) : lane;
+    const bool own_valid = t_base + tt_own < t_end;
+    const bool counts = (S::NP == 32) || lane < 32;  // head_dim 128: lanes l, l+32 share a token
+    float pw[QPK];
+#pragma unroll
+    for (int h = 0; h < QPK; ++h) {
+        const float sv = own_valid ? s[h] : -INFINITY;
+        const float m_new = fmaxf(st.m[h], wave_max(sv));
+        const float alpha = exp2f(st.m[h] - m_new);  // 0 on the first step
+        const float pl = own_valid ? exp2f(sv - m_new) : 0.f;
+        st.l[h] = st.l[h] * alpha + (counts ? pl : 0.f);
+        st.m[h] = m_new;
+        pw[h] = pl;
+        if (alpha != 1.f) {  // uniform across the wave
+            st.z[h] *= alpha;
+#pragma unroll
+            for (int c = 0; c < S::NC; ++c)
+                st.o[h][c] *= alpha;
+        }
+    }
+    const int vslot = lane / S::WPT;
+#pragma unroll
+    for (int k = 0; k < S::VTOK; ++k) {
+        const int tt = vslot + k * S::TS;
+        const uint32_t word = vwords[k];
+        const uint32_t wsh = word >> C::SHIFT;
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            const float pt = __shfl(pw[h], tt);  // 0 for absent tokens
+            const float ps = pt * lo_h(vmetas[k]);
+            st.z[h] = fmaf(pt, hi_h(vmetas[k]), st.z[h]);
+#pragma unroll
+            for (int f = 0; f < C::TPH; ++f) {
+                const uint32_t m = C::field(word, wsh, f);
+                st.o[h][f] = fmaf(ps, lo_h(m), st.o[h][f]);
+                st.o[h][C::TPH + f] = fmaf(ps, hi_h(m), st.o[h][C::TPH + f]);
+            }
+        }
+    }
+}
+
+template <int D, int KB, int VB, int QPK>
+__global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p, const void* __restrict__ q,
+                                                                float* __restrict__ out, int n,
+                                                                int splits)
+{
+    using S = Shape<D, KB, VB, QPK>;
+    using KC = Codec<KB>;
+    using VC = Codec<VB>;
+    constexpr int NP = S::NP;
+    constexpr int RS = S::RED_STRIDE;
+    extern __shared__ float smem[];  // [nwaves][64][RS] reduce buffers, reused for the merge
+    __shared__ float2 sQc[QPK][NP];
+
+    const int nwaves = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = lane % NP, gsub = lane / NP;
+    const int split = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int b = (int)(bh / p.hkv), kvh = (int)(bh % p.hkv);
+    const int ngq = n / G, tq = ngq * G, cnt_tail = n - tq;
+    const int g0 = (int)((long long)split * ngq / splits);
+    const int g1 = (int)((long long)(split + 1) * ngq / splits);
+    const bool do_tail = (split == splits - 1) && cnt_tail > 0;
+
+    // conj(q') * log2(e)/sqrt(D) for this lane's pair, q' = q rotated to n-1
+    float2 qc[QPK];
+    {
+        const int pos = n - 1;
+        const float2 rot = cmul(p.rope_group[(size_t)(pos / G) * NP + i],
+                                p.rope_offset[(pos % G) * NP + i]);
+        const float scale = kLog2e * rsqrtf((float)D);
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            const size_t qi = ((size_t)(b * p.hq + kvh * QPK + h)) * D + 2 * i;
+            const float2 qq = cmul(make_float2(ldf(q, qi, p.dtype), ldf(q, qi + 1, p.dtype)), rot);
+            qc[h] = make_float2(qq.x * scale, -qq.y * scale);
+            if (gsub == 0 && wave == 0)
+                sQc[h][i] = qc[h];
+        }
+    }
+    // per-token twiddles e^{i j theta_i}, pre-scaled by 2^(24 - pos) of the
+    // field that holds token j (j = word * 2*TPH + half * TPH + field)
+    float2 tw[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const float2 t = p.rope_offset[j * NP + i];
+        const float sc = (float)(1 << (24 - KC::pos(j % KC::TPH)));
+        tw[j] = make_float2(t.x * sc, -t.y * sc);
+    }
+
+    WaveState<QPK, S::NC> st;
+#pragma unroll
+    for (int h = 0; h < QPK; ++h) {
+        st.m[h] = -INFINITY;
+        st.l[h] = 0.f;
+        st.z[h] = 0.f;
+#pragma unroll
+        for (int c = 0; c < S::NC; ++c)
+            st.o[h][c] = 0.f;
+    }
+    float* red = smem + wave * 64 * RS;
+    const int red_half = lane & ~31, red_col = lane & 31;
+
+    HeadPlanes hp;
+    hp.kc = p.k_codes + bh * (size_t)p.gcap * D * S::WK;
+    hp.km = p.k_meta + bh * (size_t)p.gcap * D;
+    hp.vc = p.v_codes + bh * (size_t)p.tcap * S::WPT;
+    hp.vm = p.v_meta + bh * (size_t)p.tcap * S::NCG;
+    const int stride = nwaves * S::GPW;
+    StepData<KB, S::VTOK> cur, nxt;
+    int gb = g0 + wave * S::GPW;
+    if (gb < g1)
+        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
+    for (; gb < g1; gb += stride) {
+        // unconditional (clamped) prefetch: straight-line code lets the
+        // compiler wait only for the current step's loads
+        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, min(gb + stride, g1 - 1), g1, nxt);
+        const float s0 = h2f(cur.km.x), z0 = h2f(cur.km.x >> 16);
+        const float s1 = h2f(cur.km.y), z1 = h2f(cur.km.y >> 16);
+        float s[QPK];
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            const float2 Q = cmul(qc[h], cur.rg);
+            // X = P + a c0 + bb c1 = Re[Q (x+iy)],  Y = R + d c0 + e c1 = Im[Q (x+iy)]
+            const float P = Q.x * z0 - Q.y * z1, a = Q.x * s0, bb = -Q.y * s1;
+            const float R = Q.y * z0 + Q.x * z1, d = Q.y * s0, e = Q.x * s1;
+            float Ps[KC::NSCALE], Rs[KC::NSCALE];
+#pragma unroll
+            for (int k = 0; k < KC::NSCALE; ++k) {
+                const float sc = 1.0f / (float)(1 << (24 - k * KB));
+                Ps[k] = P * sc;
+                Rs[k] = R * sc;
+            }
+#pragma unroll
+            for (int w = 0; w < S::WK; ++w) {
+                const uint32_t w0 = cur.kw[w], w1 = cur.kw[S::WK + w];
+                const uint32_t w0s = w0 >> KC::SHIFT, w1s = w1 >> KC::SHIFT;
+#pragma unroll
+                for (int f = 0; f < KC::TPH; ++f) {
+                    const uint32_t m0 = KC::field(w0, w0s, f), m1 = KC::field(w1, w1s, f);
+                    const int sidx = KC::pos(f) / KB;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int j = w * 2 * KC::TPH + half * KC::TPH + f;
+                        const float c0 = half ? hi_h(m0) : lo_h(m0);
+                        const float c1 = half ? hi_h(m1) : lo_h(m1);
+                        const float X = fmaf(bb, c1, fmaf(a, c0, Ps[sidx]));
+                        const float Y = fmaf(e, c1, fmaf(d, c0, Rs[sidx]));
+                        red[lane * RS + j] = fmaf(tw[j].x, X, tw[j].y * Y);
+                    }
+                }
+            }
+            float a4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+#pragma unroll
+            for (int m = 0; m < 32; ++m)
+                a4[m & 3] += red[(red_half + m) * RS + red_col];
+            float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+            if (NP == 64)
+                acc += __shfl_xor(acc, 32);
+            s[h] = acc;
+        }
+        softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, cur.vw, cur.vm, st);
+        cur = nxt;
+    }
+
+    if (do_tail) {
+        __syncthreads();  // sQc written by wave 0
+        if (wave == nwaves - 1) {
+            const int tt = (NP == 64) ? (lane & 31) : lane;
+            float s[QPK];
+#pragma unroll
+            for (int h = 0; h < QPK; ++h)
+                s[h] = 0.f;
+            if (tt < cnt_tail) {
+                const size_t trow = (bh * G + tt) * D;
+                for (int ii = 0; ii < NP; ++ii) {
+                    const float2 rot = cmul(p.rope_group[(size_t)ngq * NP + ii],
+                                            p.rope_offset[tt * NP + ii]);
+                    const float2 kr = cmul(make_float2(ldf(p.k_tail, trow + 2 * ii, p.dtype),
+                                                       ldf(p.k_tail, trow + 2 * ii + 1, p.dtype)),
+                                           rot);
+#pragma unroll
+                    for (int h = 0; h < QPK; ++h) {
+                        const float2 qv = sQc[h][ii];
+                        s[h] += qv.x * kr.x - qv.y * kr.y;
+                    }
+                }
+            }
+            uint32_t vw[S::VTOK], vm[S::VTOK];
+            const int vwi = lane % S::WPT, vslot = lane / S::WPT, vcg = vwi / S::WV;
+#pragma unroll
+            for (int k = 0; k < S::VTOK; ++k) {
+                const unsigned t = (unsigned)min(tq + vslot + k * S::TS, n - 1);
+                vw[k] = hp.vc[t * S::WPT + vwi];
+                vm[k] = hp.vm[t * S::NCG + vcg];
+            }
+            softmax_values<D, KB, VB, QPK>(lane, tq, n, s, vw, vm, st);
+        }
+    }
+
+    // ---- merge the waves of this block
+    __syncthreads();  // every wave is done with its reduce buffer
+    float* sm = smem;                           // [nwaves][QPK]
+    float* sl = smem + kMaxWaves * QPK;         // [nwaves][QPK]
+    float* so = smem + 2 * kMaxWaves * QPK;     // [nwaves][QPK][D]
+    {
+        const int vw = lane % S::WPT, vslot = lane / S::WPT;
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            const float L = wave_sum(st.l[h]);
+            float v[S::NC];
+#pragma unroll
+            for (int c = 0; c < S::NC; ++c) {
+                // undo the field scale 2^(pos-24) of channel c of the word
+                const float sc = (float)(1 << (24 - VC::pos(c % VC::TPH)));
+                float x = fmaf(st.o[h][c], sc, st.z[h]);
+#pragma unroll
+                for (int off = S::WPT; off < 64; off <<= 1)
+                    x += __shfl_xor(x, off);
+                v[c] = x;
+            }
+            if (vslot == 0) {
+#pragma unroll
+                for (int c = 0; c < S::NC; ++c)
+                    so[(wave * QPK + h) * D + vw * S::NC + c] = v[c];
+            }
+            if (lane == 0) {
+                sm[wave * QPK + h] = st.m[h];
+                sl[wave * QPK + h] = L;
+            }
+        }
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
+    const bool single = (splits == 1);
+    for (int idx = tid; idx < QPK * D; idx += blockDim.x) {
+        const int h = idx / D, c = idx % D;
+        float M = -INFINITY;
+        for (int w = 0; w < nwaves; ++w)
+            M = fmaxf(M, sm[w * QPK + h]);
+        float L = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+            for (int w = 0; w < nwaves; ++w) {
+                const float f = exp2f(sm[w * QPK + h] - M);
+                L += f * sl[w * QPK + h];
+                acc += f * so[(w * QPK + h) * D + c];
+            }
+        }
+        const size_t row = (size_t)b * p.hq + kvh * QPK + h;
+        if (single) {
+            out[row * D + c] = acc / L;
+        } else {
+            float* dst = p.partials + (row * p.max_splits + split) * (D + 2);
+            dst[c] = acc;
+            if (c == 0) {
+                dst[D] = M;
+                dst[D + 1] = L;
+            }
+        }
+    }
+}
+
+// Merge the split partials of one output row (grid: batch * q_heads rows,
+// head_dim threads): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// A split whose m is -inf saw no tokens and is skipped.
+template <int D>
+__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ partials,
+                                                    int max_splits, int splits,
+                                                    float* __restrict__ out)
+{
+    const size_t row = blockIdx.x;
+    const int c = threadIdx.x;
+    const float* base = partials + row * max_splits * (D + 2);
+    float M = -INFINITY;
+    for (int sp = 0; sp < splits; ++sp)
+        M = fmaxf(M, base[sp * (D + 2) + D]);
+    float L = 0.f, acc = 0.f;
+    for (int sp = 0; sp < splits; ++sp) {
+        const float ms = base[sp * (D + 2) + D];
+        if (ms == -INFINITY)
+            continue;
+        const float f = exp2f(ms - M);
+        L += f * base[sp * (D + 2) + D + 1];
+        acc += f * base[sp * (D + 2) + c];
+    }
+    out[row * D + c] = acc / L;
+}
+
+// Bytes of dynamic LDS for a block of nwaves waves.
+template <int D, int KB, int VB, int QPK>
+constexpr size_t attend_lds_bytes(int nwaves)
+{
+    using S = Shape<D, KB, VB, QPK>;
+    const size_t red = (size_t)nwaves * 64 * S::RED_STRIDE;
+    const size_t merge = 2 * kMaxWaves * QPK + (size_t)nwaves * QPK * D;
+    return 4 * (red > merge ? red : merge);
+}
+
+template <int D, int KB, int VB, int QPK>
+void launch(const Planes& p, const void* q, float* out, int n, int splits, int nwaves,
+            hipStream_t stream)
+{
+    dim3 grid(splits, p.nb * p.hkv);
+    nwaves = nwaves < max_waves<QPK>() ? nwaves : max_waves<QPK>();
+    attend_kernel<D, KB, VB, QPK><<<grid, 64 * nwaves, attend_lds_bytes<D, KB, VB, QPK>(nwaves),
+                                    stream>>>(p, q, out, n, splits);
+    if (splits > 1)
+        combine_kernel<D><<<p.nb * p.hq, D, 0, stream>>>(p.partials, p.max_splits, splits, out);
+}
+
+template <int D, int KB, int VB>
+void by_qpk(const Planes& p, const void* q, float* out, int n, int splits, int nwaves,
+            hipStream_t s)
+{
+    switch (p.hq / p.hkv) {
+    case 1: launch<D, KB, VB, 1>(p, q, out, n, splits, nwaves, s); break;
+    case 2: launch<D, KB, VB, 2>(p, q, out, n, splits, nwaves, s); break;
+    case 4: launch<D, KB, VB, 4>(p, q, out, n, splits, nwaves, s); break;
+    case 8: launch<D, KB, VB, 8>(p, q, out, n, splits, nwaves, s); break;
+    }
+}
+
+template <int D, int KB>
+void by_vb(const Planes& p, const void* q, float* out, int n, int splits, int nwaves,
+           hipStream_t s)
+{
+    switch (p.vbits) {
+    case 2: by_qpk<D, KB, 2>(p, q, out, n, splits, nwaves, s); break;
+    case 4: by_qpk<D, KB, 4>(p, q, out, n, splits, nwaves, s); break;
+    case 8: by_qpk<D, KB, 8>(p, q, out, n, splits, nwaves, s); break;
+    }
+}
+
+template <int D>
+hipError_t launch_attend_d(const Planes& p, const void* q, float* out, int n, int splits,
+                           int nwaves, hipStream_t s)
+{
+    switch (p.kbits) {
+    case 2: by_vb<D, 2>(p, q, out, n, splits, nwaves, s); break;
+    case 4: by_vb<D, 4>(p, q, out, n, splits, nwaves, s); break;
+    case 8: by_vb<D, 8>(p, q, out, n, splits, nwaves, s); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace kvqi

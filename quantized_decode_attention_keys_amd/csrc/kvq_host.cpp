@@ -14,6 +14,9 @@ struct kvq {
     kvq_layout layout;
     char* ws;
     int32_t n;
+    int32_t cus;            // compute units of the device the handle was made on
+    int32_t force_splits;   // tuning overrides (KVQ_ATTEND_SPLITS / KVQ_ATTEND_WAVES), 0 = auto
+    int32_t force_waves;
 };
 
 namespace {
@@ -41,7 +44,7 @@ int check_config(const kvq_config* c)
         return KVQ_ERR_UNSUPPORTED;
     // keep every plane index inside 2^31 elements per (sequence, head) and
     // the grid dimensions inside their limits
-    if ((long long)c->max_tokens > (1LL << 26) || (long long)c->batch * c->q_heads > (1LL << 24) ||
+    if ((long long)c->max_tokens > (1LL << 24) || (long long)c->batch * c->q_heads > (1LL << 24) ||
         (long long)c->batch * c->kv_heads > 65535)
         return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
@@ -68,7 +71,6 @@ void make_layout(const kvq_config* c, kvq_layout* L)
     L->rope_group = off; off = align_up(off + (size_t)gcap * (D / 2) * 8);
     L->rope_offset = off; off = align_up(off + G * (D / 2) * 8);
     L->partials = off;  off = align_up(off + nb * hq * (size_t)ms * (D + 2) * 4);
-    L->counters = off;  off = align_up(off + nb * hq * 4);
     L->total_bytes = off;
     L->gcap = gcap;
     L->tcap = (int32_t)tcap;
@@ -87,7 +89,6 @@ kvqi::Planes planes_of(const kvq* h)
     p.rope_group = reinterpret_cast<const float2*>(h->ws + L.rope_group);
     p.rope_offset = reinterpret_cast<const float2*>(h->ws + L.rope_offset);
     p.partials = reinterpret_cast<float*>(h->ws + L.partials);
-    p.counters = reinterpret_cast<uint32_t*>(h->ws + L.counters);
     p.nb = h->cfg.batch;
     p.hq = h->cfg.q_heads;
     p.hkv = h->cfg.kv_heads;
@@ -102,6 +103,51 @@ kvqi::Planes planes_of(const kvq* h)
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+int env_int(const char* name)
+{
+    const char* v = std::getenv(name);
+    return v ? std::atoi(v) : 0;
+}
+
+// Launch shape of the decode-attention kernel.  Enough waves to fill every
+// compute unit (about 12 resident per CU at the kernel's register use) without
+// splitting a (sequence, KV head) when there are at least as many of those
+// as CUs; otherwise split the token range and merge the partials.
+void attend_shape(const kvq* h, int n, int* splits_out, int* waves_out)
+{
+    constexpr int kWavesPerCu = 12;
+    const int units = h->cfg.batch * h->cfg.kv_heads;
+    const int cus = h->cus > 0 ? h->cus : 256;
+    const int full_groups = n / h->cfg.group;
+    const int groups_per_step = 64 / (h->cfg.head_dim / 2);
+    int splits, waves;
+    if (units >= cus) {
+        splits = 1;
+        waves = kWavesPerCu * cus / units;
+    } else {
+        splits = (2 * cus + units - 1) / units;
+        waves = kWavesPerCu / 2;
+    }
+    if (h->force_splits > 0)
+        splits = h->force_splits;
+    if (splits > h->layout.max_splits)
+        splits = h->layout.max_splits;
+    if (splits > full_groups)
+        splits = full_groups > 0 ? full_groups : 1;
+    const int per_block = (full_groups + splits - 1) / splits;
+    const int useful = (per_block + groups_per_step - 1) / groups_per_step;
+    if (waves > useful)
+        waves = useful;
+    if (h->force_waves > 0)
+        waves = h->force_waves;
+    if (waves > 12)
+        waves = 12;  // the kernel's block limit
+    if (waves < 1)
+        waves = 1;
+    *splits_out = splits;
+    *waves_out = waves;
+}
 
 }  // namespace
 
@@ -160,7 +206,8 @@ int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes, kvq_t** out)
     if (hipMemcpy(ws + L.rope_group, grp.data(), grp.size() * sizeof(float),
                   hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ws + L.rope_offset, offs.data(), offs.size() * sizeof(float),
-                  hipMemcpyHostToDevice) != hipSuccess)
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
         return KVQ_ERR_HIP;
     kvq* h = new (std::nothrow) kvq;
     if (!h)
@@ -169,6 +216,13 @@ int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes, kvq_t** out)
     h->layout = L;
     h->ws = ws;
     h->n = 0;
+    h->cus = 0;
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+        h->cus = prop.multiProcessorCount;
+    h->force_splits = env_int("KVQ_ATTEND_SPLITS");
+    h->force_waves = env_int("KVQ_ATTEND_WAVES");
     *out = h;
     return KVQ_OK;
 }
@@ -213,12 +267,13 @@ int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream)
     if (h->n == 0)
         return KVQ_ERR_STATE;
     const int n = h->n;
-    const int units = n / h->cfg.group + (n % h->cfg.group ? 1 : 0);
-    int splits = h->layout.max_splits;
-    if (splits > units)
-        splits = units;
-    return hip_status(kvqi::launch_attend(planes_of(h), d_q, d_out, n, splits,
-                                         static_cast<hipStream_t>(stream)));
+    int splits, waves;
+    attend_shape(h, n, &splits, &waves);
+    const kvqi::Planes p = planes_of(h);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(h->cfg.head_dim == 64
+                          ? kvqi::launch_attend_d64(p, d_q, d_out, n, splits, waves, s)
+                          : kvqi::launch_attend_d128(p, d_q, d_out, n, splits, waves, s));
 }
 
 int kvq_destroy(kvq_t* h)

@@ -20,7 +20,6 @@ struct Planes {
     const float2* rope_group;   // [gcap][D/2]  (cos, sin) of g*G*theta_i
     const float2* rope_offset;  // [G][D/2]     (cos, sin) of j*theta_i
     float* partials;     // [nb*hq][max_splits][D+2]
-    uint32_t* counters;  // [nb*hq]
     int nb, hq, hkv, D, kbits, vbits, gcap, tcap, max_splits, dtype;
 };
 
@@ -30,7 +29,9 @@ hipError_t launch_quantize_prefill(const Planes& p, const void* k, const void* v
                                    int n_tokens, hipStream_t stream);
 hipError_t launch_append(const Planes& p, const void* k, const void* v, int n,
                          hipStream_t stream);
-hipError_t launch_attend(const Planes& p, const void* q, float* out, int n,
-                         int splits, hipStream_t stream);
+hipError_t launch_attend_d64(const Planes& p, const void* q, float* out, int n,
+                             int splits, int waves, hipStream_t stream);
+hipError_t launch_attend_d128(const Planes& p, const void* q, float* out, int n,
+                              int splits, int waves, hipStream_t stream);
 
 }  // namespace kvqi

@@ -1,5 +1,5 @@
-// kvq_kernels.hip -- gfx950 kernels: key/value quantize-and-pack, key-tail
-// append and flush, decode attention over the quantized cache, split combine.
+// kvq_kernels.hip -- gfx950 kernels: key/value quantize-and-pack and the
+// key-tail append and flush (decode attention lives in kvq_attend.hip).
 //
 // Method (web pages): uniform asymmetric integer codes per group, zero point
 // = group minimum, step = range/(2^B-1), nearest step ("Your KV Cache Doesn't
@@ -134,19 +134,37 @@ __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __
     p.v_meta[tc] = meta;
 }
 
-// Append one key per sequence/head into tail slot n mod G; when that slot is
-// the last one, quantize the full tail as key group n/G.  One thread per
-// channel: every tail element a thread reads was written by the same
-// thread's channel (this launch) or by an earlier launch.
-template <typename T, int BITS>
-__global__ void append_keys_kernel(Planes p, const T* __restrict__ k, int n)
+// Append one token per sequence/head in one launch (block = one sequence/head,
+// head_dim threads).  Keys: thread c writes channel c into tail slot n mod G
+// and, when that slot is the last one, quantizes the full tail as key group
+// n/G; every tail element it reads was written by the same thread (this
+// launch) or by an earlier launch.  Values: threads c < D/G each quantize
+// channel group c of the new value row into cache slot n.
+template <typename T, int KBITS, int VBITS>
+__global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __restrict__ v, int n)
 {
-    constexpr int WK = G * BITS / 32;
+    constexpr int WK = G * KBITS / 32, WV = G * VBITS / 32;
     const int D = p.D;
     const int c = threadIdx.x;
     const size_t bh = blockIdx.x;
     if (c >= D)
         return;
+    const int ncg = D / G;
+    if (c < ncg) {
+        float x[G];
+        const T* src = v + bh * D + (size_t)c * G;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            x[j] = to_f32(src[j]);
+        uint32_t w[WV];
+        const uint32_t meta = quantize_pack<VBITS>(x, w);
+        const size_t tc = (bh * p.tcap + n) * ncg + c;
+        uint32_t* dst = p.v_codes + tc * WV;
+#pragma unroll
+        for (int i = 0; i < WV; ++i)
+            dst[i] = w[i];
+        p.v_meta[tc] = meta;
+    }
     T* tail = reinterpret_cast<T*>(p.k_tail);
     const int slot = n % G;
     const T val = k[bh * D + c];
@@ -159,201 +177,13 @@ __global__ void append_keys_kernel(Planes p, const T* __restrict__ k, int n)
         x[j] = to_f32(tail[(bh * G + j) * D + c]);
     x[G - 1] = to_f32(val);
     uint32_t w[WK];
-    const uint32_t meta = quantize_pack<BITS>(x, w);
+    const uint32_t meta = quantize_pack<KBITS>(x, w);
     const size_t gc = (bh * p.gcap + n / G) * D + c;
     uint32_t* dst = p.k_codes + gc * WK;
 #pragma unroll
     for (int i = 0; i < WK; ++i)
         dst[i] = w[i];
     p.k_meta[gc] = meta;
-}
-
-// ------------------------------------------------------ decode attention --
-
-__device__ __forceinline__ float2 cmul(float2 a, float2 b)
-{
-    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
-}
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Reference-structured decode attention (one block per (split, sequence*KV
-// head)).  Each block walks its token units (a unit = one key group of G
-// tokens, or the tail), computes the scores of every query head that reads
-// this KV head, keeps an online softmax (running max m and sum l, base 2),
-// accumulates sum p*vhat, and writes (o[D], m, l) to its partial slot.
-template <int D, int KB, int VB, typename T>
-__global__ __launch_bounds__(256) void attend_ref_kernel(Planes p, const T* __restrict__ q, int n,
-                                                         int splits)
-{
-    constexpr int NP = D / 2;
-    constexpr int WK = G * KB / 32, WV = G * VB / 32, NCG = D / G;
-    constexpr int PARTS = 256 / G;          // threads per token in the score pass
-    constexpr int PPP = NP / PARTS;         // pairs per thread
-    constexpr int MAXQ = 8;
-    const int tid = threadIdx.x;
-    const int split = blockIdx.x;
-    const int bh = blockIdx.y;
-    const int b = bh / p.hkv, kvh = bh % p.hkv;
-    const int qpk = p.hq / p.hkv;
-    const int ngq = n / G;
-    const int tq = ngq * G;
-    const bool has_tail = n > tq;
-    const int units = ngq + (has_tail ? 1 : 0);
-    const int u0 = (int)((long long)split * units / splits);
-    const int u1 = (int)((long long)(split + 1) * units / splits);
-
-    __shared__ float2 sQ[MAXQ][NP];
-    __shared__ float sP[MAXQ][G];
-    __shared__ float sAlpha[MAXQ];
-
-    // conj(rotated query) * log2(e)/sqrt(D)
-    {
-        const int pos = n - 1;
-        const float scale = kLog2e * rsqrtf((float)D);
-        for (int idx = tid; idx < qpk * NP; idx += blockDim.x) {
-            const int hh = idx / NP, i = idx % NP;
-            const float2 rot = cmul(p.rope_group[(size_t)(pos / G) * NP + i],
-                                    p.rope_offset[(pos % G) * NP + i]);
-            const T* qp = q + ((size_t)(b * p.hq + kvh * qpk + hh)) * D + 2 * i;
-            const float2 qq = cmul(make_float2(to_f32(qp[0]), to_f32(qp[1])), rot);
-            sQ[hh][i] = make_float2(qq.x * scale, -qq.y * scale);
-        }
-    }
-    __syncthreads();
-
-    float m_run[MAXQ], l_run[MAXQ];
-    for (int hh = 0; hh < MAXQ; ++hh) {
-        m_run[hh] = -INFINITY;
-        l_run[hh] = 0.f;
-    }
-    constexpr int MAXCOMBO = MAXQ * D / 256;
-    float o[MAXCOMBO];
-    for (int r = 0; r < MAXCOMBO; ++r)
-        o[r] = 0.f;
-
-    const T* tail = reinterpret_cast<const T*>(p.k_tail) + (size_t)bh * G * D;
-    for (int u = u0; u < u1; ++u) {
-        const bool tail_unit = (u == ngq);
-        const int cnt = tail_unit ? n - tq : G;
-        const int t0 = u * G;
-        // ---- scores: thread (j, part)
-        const int j = tid / PARTS, part = tid % PARTS;
-        float sc[MAXQ];
-        for (int hh = 0; hh < MAXQ; ++hh)
-            sc[hh] = 0.f;
-        if (j < cnt) {
-            for (int ii = 0; ii < PPP; ++ii) {
-                const int i = part * PPP + ii;
-                float x, y;
-                if (tail_unit) {
-                    x = to_f32(tail[(size_t)j * D + 2 * i]);
-                    y = to_f32(tail[(size_t)j * D + 2 * i + 1]);
-                } else {
-                    const size_t gc = ((size_t)bh * p.gcap + u) * D + 2 * i;
-                    const int bit = j * KB;
-                    const uint32_t c0 = (p.k_codes[gc * WK + bit / 32] >> (bit % 32)) & ((1u << KB) - 1u);
-                    const uint32_t c1 = (p.k_codes[(gc + 1) * WK + bit / 32] >> (bit % 32)) & ((1u << KB) - 1u);
-                    const uint32_t m0 = p.k_meta[gc], m1 = p.k_meta[gc + 1];
-                    x = half_bits_to_float(m0 >> 16) + half_bits_to_float(m0 & 0xffffu) * (float)c0;
-                    y = half_bits_to_float(m1 >> 16) + half_bits_to_float(m1 & 0xffffu) * (float)c1;
-                }
-                const float2 rot = cmul(p.rope_group[(size_t)u * NP + i], p.rope_offset[j * NP + i]);
-                const float2 kr = cmul(make_float2(x, y), rot);
-                for (int hh = 0; hh < qpk; ++hh) {
-                    const float2 qc = sQ[hh][i];
-                    sc[hh] += qc.x * kr.x - qc.y * kr.y;  // Re[conj(q') k']
-                }
-            }
-        }
-        for (int hh = 0; hh < qpk; ++hh) {
-            float s = sc[hh];
-            for (int off = 1; off < PARTS; off <<= 1)
-                s += __shfl_xor(s, off);
-            sc[hh] = s;
-        }
-        // ---- online softmax: every thread of a head row sees all scores
-        __shared__ float sS[MAXQ][G];
-        if (part == 0)
-            for (int hh = 0; hh < qpk; ++hh)
-                sS[hh][j] = (j < cnt) ? sc[hh] : -INFINITY;
-        __syncthreads();
-        if (tid < qpk) {
-            const int hh = tid;
-            float mx = m_run[hh];
-            for (int jj = 0; jj < cnt; ++jj)
-                mx = fmaxf(mx, sS[hh][jj]);
-            sAlpha[hh] = exp2f(m_run[hh] - mx);  // 0 on the first unit
-            float sum = 0.f;
-            for (int jj = 0; jj < G; ++jj) {
-                const float pj = (jj < cnt) ? exp2f(sS[hh][jj] - mx) : 0.f;
-                sP[hh][jj] = pj;
-                sum += pj;
-            }
-            sS[hh][0] = mx;  // broadcast the new max (scores no longer needed)
-            sS[hh][1] = sum;
-        }
-        __syncthreads();
-        for (int hh = 0; hh < qpk; ++hh) {
-            l_run[hh] = l_run[hh] * sAlpha[hh] + sS[hh][1];
-            m_run[hh] = sS[hh][0];
-        }
-        // ---- values: thread owns (head, channel) combos
-        for (int r = 0; r < MAXCOMBO; ++r) {
-            const int combo = tid + r * 256;
-            if (combo >= qpk * D)
-                break;
-            const int hh = combo / D, c = combo % D;
-            const int cg = c / G, jc = c % G;
-            float acc = o[r] * sAlpha[hh];
-            for (int jj = 0; jj < cnt; ++jj) {
-                const size_t tc = ((size_t)bh * p.tcap + t0 + jj) * NCG + cg;
-                const int bit = jc * VB;
-                const uint32_t code = (p.v_codes[tc * WV + bit / 32] >> (bit % 32)) & ((1u << VB) - 1u);
-                const uint32_t mt = p.v_meta[tc];
-                const float vh = half_bits_to_float(mt >> 16) + half_bits_to_float(mt & 0xffffu) * (float)code;
-                acc += sP[hh][jj] * vh;
-            }
-            o[r] = acc;
-        }
-        __syncthreads();
-    }
-    // ---- partials
-    for (int r = 0; r < MAXCOMBO; ++r) {
-        const int combo = tid + r * 256;
-        if (combo >= qpk * D)
-            break;
-        const int hh = combo / D, c = combo % D;
-        const size_t row = (size_t)b * p.hq + kvh * qpk + hh;
-        float* dst = p.partials + (row * p.max_splits + split) * (D + 2);
-        dst[c] = o[r];
-        if (c == 0) {
-            dst[D] = m_run[hh];
-            dst[D + 1] = l_run[hh];
-        }
-    }
-}
-
-// Merge the split partials of one output row: out = sum_s 2^(m_s-M) o_s /
-// sum_s 2^(m_s-M) l_s.
-__global__ void combine_kernel(const float* __restrict__ partials, int max_splits, int splits,
-                               int D, float* __restrict__ out)
-{
-    const size_t row = blockIdx.x;
-    const int c = threadIdx.x;
-    const float* base = partials + row * max_splits * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s)
-        M = fmaxf(M, base[s * (D + 2) + D]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        const float w = exp2f(base[s * (D + 2) + D] - M);
-        L += w * base[s * (D + 2) + D + 1];
-        if (c < D)
-            acc += w * base[s * (D + 2) + c];
-    }
-    if (c < D)
-        out[row * D + c] = acc / L;
 }
 
 // ------------------------------------------------------------- dispatch --
@@ -388,50 +218,26 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
     return hipGetLastError();
 }
 
+template <typename T, int KBITS>
+void append_kb(const Planes& p, const T* k, const T* v, int n, hipStream_t stream)
+{
+    const int nbh = p.nb * p.hkv;
+    switch (p.vbits) {
+    case 2: append_kernel<T, KBITS, 2><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+    case 4: append_kernel<T, KBITS, 4><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+    case 8: append_kernel<T, KBITS, 8><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+    }
+}
+
 template <typename T>
 hipError_t append_t(const Planes& p, const T* k, const T* v, int n, hipStream_t stream)
 {
-    const int nbh = p.nb * p.hkv;
     switch (p.kbits) {
-    case 2: append_keys_kernel<T, 2><<<nbh, p.D, 0, stream>>>(p, k, n); break;
-    case 4: append_keys_kernel<T, 4><<<nbh, p.D, 0, stream>>>(p, k, n); break;
-    case 8: append_keys_kernel<T, 8><<<nbh, p.D, 0, stream>>>(p, k, n); break;
-    }
-    const size_t vg = (size_t)nbh * (p.D / G);
-    const unsigned vblocks = (unsigned)((vg + 255) / 256);
-    switch (p.vbits) {
-    case 2: quant_values_kernel<T, 2><<<vblocks, 256, 0, stream>>>(p, v, 1, n, vg); break;
-    case 4: quant_values_kernel<T, 4><<<vblocks, 256, 0, stream>>>(p, v, 1, n, vg); break;
-    case 8: quant_values_kernel<T, 8><<<vblocks, 256, 0, stream>>>(p, v, 1, n, vg); break;
+    case 2: append_kb<T, 2>(p, k, v, n, stream); break;
+    case 4: append_kb<T, 4>(p, k, v, n, stream); break;
+    case 8: append_kb<T, 8>(p, k, v, n, stream); break;
     }
     return hipGetLastError();
-}
-
-template <int D, int KB, int VB, typename T>
-void attend_launch(const Planes& p, const void* q, int n, int splits, hipStream_t stream)
-{
-    dim3 grid(splits, p.nb * p.hkv);
-    attend_ref_kernel<D, KB, VB, T><<<grid, 256, 0, stream>>>(p, static_cast<const T*>(q), n, splits);
-}
-
-template <int D, int KB, typename T>
-void attend_vb(const Planes& p, const void* q, int n, int splits, hipStream_t s)
-{
-    switch (p.vbits) {
-    case 2: attend_launch<D, KB, 2, T>(p, q, n, splits, s); break;
-    case 4: attend_launch<D, KB, 4, T>(p, q, n, splits, s); break;
-    case 8: attend_launch<D, KB, 8, T>(p, q, n, splits, s); break;
-    }
-}
-
-template <int D, typename T>
-void attend_kb(const Planes& p, const void* q, int n, int splits, hipStream_t s)
-{
-    switch (p.kbits) {
-    case 2: attend_vb<D, 2, T>(p, q, n, splits, s); break;
-    case 4: attend_vb<D, 4, T>(p, q, n, splits, s); break;
-    case 8: attend_vb<D, 8, T>(p, q, n, splits, s); break;
-    }
 }
 
 }  // namespace
@@ -452,20 +258,6 @@ hipError_t launch_append(const Planes& p, const void* k, const void* v, int n, h
         return append_t<__half>(p, static_cast<const __half*>(k), static_cast<const __half*>(v), n,
                                 stream);
     return append_t<float>(p, static_cast<const float*>(k), static_cast<const float*>(v), n, stream);
-}
-
-hipError_t launch_attend(const Planes& p, const void* q, float* out, int n, int splits,
-                         hipStream_t stream)
-{
-    if (p.D == 64) {
-        if (p.dtype == 0) attend_kb<64, __half>(p, q, n, splits, stream);
-        else attend_kb<64, float>(p, q, n, splits, stream);
-    } else {
-        if (p.dtype == 0) attend_kb<128, __half>(p, q, n, splits, stream);
-        else attend_kb<128, float>(p, q, n, splits, stream);
-    }
-    combine_kernel<<<p.nb * p.hq, p.D, 0, stream>>>(p.partials, p.max_splits, splits, p.D, out);
-    return hipGetLastError();
 }
 
 }  // namespace kvqi

@@ -49,7 +49,7 @@ def test_layout_sizes_alignment_and_order():
     assert st == L.KVQ_OK
     assert lay.gcap == 32 and lay.tcap == 1024
     offs = [lay.k_codes, lay.k_meta, lay.v_codes, lay.v_meta, lay.k_tail, lay.rope_group,
-            lay.rope_offset, lay.partials, lay.counters, lay.total_bytes]
+            lay.rope_offset, lay.partials, lay.total_bytes]
     assert offs == sorted(offs)
     assert all(o % 256 == 0 for o in offs)
     nb, h, D = 2, 2, 128
