@@ -278,7 +278,6 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
     constexpr int NP = S::NP;
     constexpr int RS = S::RED_STRIDE;
     extern __shared__ float smem[];  // [nwaves][64][RS] reduce buffers, reused for the merge
-    __shared__ float2 sQc[QPK][NP];
 
     const int nwaves = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -303,8 +302,6 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
             const size_t qi = ((size_t)(b * p.hq + kvh * QPK + h)) * D + 2 * i;
             const float2 qq = cmul(make_float2(ldf(q, qi, p.dtype), ldf(q, qi + 1, p.dtype)), rot);
             qc[h] = make_float2(qq.x * scale, -qq.y * scale);
-            if (gsub == 0 && wave == 0)
-                sQc[h][i] = qc[h];
         }
     }
     // per-token twiddles e^{i j theta_i}, pre-scaled by 2^(24 - pos) of the
@@ -340,6 +337,66 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
     int gb = g0 + wave * S::GPW;
     if (gb < g1)
         load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
+
+    if (do_tail && wave == nwaves - 1) {
+        // The tail (cnt_tail < G unquantized keys, slot j = token tq + j) is
+        // scored like one more group by the wave with the fewest groups:
+        // lane = channel pair, the tail tokens across the lane's registers.
+        uint32_t vw[S::VTOK], vm[S::VTOK];
+        {
+            const int vwi = lane % S::WPT, vslot = lane / S::WPT, vcg = vwi / S::WV;
+#pragma unroll
+            for (int k = 0; k < S::VTOK; ++k) {
+                const unsigned t = (unsigned)min(tq + vslot + k * S::TS, n - 1);
+                vw[k] = hp.vc[t * S::WPT + vwi];
+                vm[k] = hp.vm[t * S::NCG + vcg];
+            }
+        }
+        float tx[G], ty[G];
+        const size_t trow = (bh * G) * D + 2 * i;  // element index of (slot 0, channel 2i)
+        if (p.dtype == 0) {
+            const uint32_t* t32 = reinterpret_cast<const uint32_t*>(p.k_tail) + trow / 2;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const uint32_t w = (gsub == 0 && j < cnt_tail) ? t32[(size_t)j * (D / 2)] : 0u;
+                tx[j] = lo_h(w);
+                ty[j] = hi_h(w);
+            }
+        } else {
+            const float2* t64 = reinterpret_cast<const float2*>(p.k_tail) + trow / 2;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float2 w = (gsub == 0 && j < cnt_tail) ? t64[(size_t)j * (D / 2)]
+                                                             : make_float2(0.f, 0.f);
+                tx[j] = w.x;
+                ty[j] = w.y;
+            }
+        }
+        const float2 rg = p.rope_group[(size_t)ngq * NP + i];
+        float s[QPK];
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            const float2 Q = cmul(qc[h], rg);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                // Re[T_j Q (x + iy)]; tw[j] carries (T.x, -T.y) * 2^(24-pos)
+                const float vr = Q.x * tx[j] - Q.y * ty[j];
+                const float vi = Q.x * ty[j] + Q.y * tx[j];
+                const float unscale = 1.0f / (float)(1 << (24 - KC::pos(j % KC::TPH)));
+                red[lane * RS + j] = fmaf(tw[j].x, vr, tw[j].y * vi) * unscale;
+            }
+            float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 32; ++m)
+                a4[m & 3] += red[(red_half + m) * RS + red_col];
+            float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+            if (NP == 64)
+                acc += __shfl_xor(acc, 32);
+            s[h] = acc;
+        }
+        softmax_values<D, KB, VB, QPK>(lane, tq, n, s, vw, vm, st);
+    }
+
     for (; gb < g1; gb += stride) {
         // unconditional (clamped) prefetch: straight-line code lets the
         // compiler wait only for the current step's loads
@@ -390,41 +447,6 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
         }
         softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, cur.vw, cur.vm, st);
         cur = nxt;
-    }
-
-    if (do_tail) {
-        __syncthreads();  // sQc written by wave 0
-        if (wave == nwaves - 1) {
-            const int tt = (NP == 64) ? (lane & 31) : lane;
-            float s[QPK];
-#pragma unroll
-            for (int h = 0; h < QPK; ++h)
-                s[h] = 0.f;
-            if (tt < cnt_tail) {
-                const size_t trow = (bh * G + tt) * D;
-                for (int ii = 0; ii < NP; ++ii) {
-                    const float2 rot = cmul(p.rope_group[(size_t)ngq * NP + ii],
-                                            p.rope_offset[tt * NP + ii]);
-                    const float2 kr = cmul(make_float2(ldf(p.k_tail, trow + 2 * ii, p.dtype),
-                                                       ldf(p.k_tail, trow + 2 * ii + 1, p.dtype)),
-                                           rot);
-#pragma unroll
-                    for (int h = 0; h < QPK; ++h) {
-                        const float2 qv = sQc[h][ii];
-                        s[h] += qv.x * kr.x - qv.y * kr.y;
-                    }
-                }
-            }
-            uint32_t vw[S::VTOK], vm[S::VTOK];
-            const int vwi = lane % S::WPT, vslot = lane / S::WPT, vcg = vwi / S::WV;
-#pragma unroll
-            for (int k = 0; k < S::VTOK; ++k) {
-                const unsigned t = (unsigned)min(tq + vslot + k * S::TS, n - 1);
-                vw[k] = hp.vc[t * S::WPT + vwi];
-                vm[k] = hp.vm[t * S::NCG + vcg];
-            }
-            softmax_values<D, KB, VB, QPK>(lane, tq, n, s, vw, vm, st);
-        }
     }
 
     // ---- merge the waves of this block

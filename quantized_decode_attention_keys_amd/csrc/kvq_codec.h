@@ -103,11 +103,8 @@ KVQ_HD uint32_t code_of(double x, const GroupParams& g, int top)
     const double d = x - g.z;
     double c = rint(d * g.rinv);
     const double e = fma(-c, g.s, d);
-    if (2.0 * fabs(e) == g.s) {
-        const double other = c + (e > 0.0 ? 1.0 : -1.0);
-        if (fmod(c, 2.0) != 0.0)
-            c = other;
-    }
+    if (2.0 * fabs(e) == g.s && ((long long)c & 1))  // exact tie, c odd: take the even neighbour
+        c += (e > 0.0 ? 1.0 : -1.0);
     c = fmin(fmax(c, 0.0), (double)top);
     return (uint32_t)c;
 }

@@ -135,35 +135,44 @@ __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __
 }
 
 // Append one token per sequence/head in one launch (block = one sequence/head,
-// head_dim threads).  Keys: thread c writes channel c into tail slot n mod G
-// and, when that slot is the last one, quantizes the full tail as key group
-// n/G; every tail element it reads was written by the same thread (this
-// launch) or by an earlier launch.  Values: threads c < D/G each quantize
-// channel group c of the new value row into cache slot n.
+// head_dim threads, thread c = channel c).
+// Values: the 32 lanes of a channel group find the group's min and max with
+// lane shuffles, each codes its own element, and the codes are OR-reduced
+// into 32-bit words across the lanes that share a word.
+// Keys: thread c writes channel c into tail slot n mod G and, when that slot
+// is the last one, quantizes the full tail as key group n/G; every tail
+// element it reads was written by the same thread (this launch) or by an
+// earlier launch.
 template <typename T, int KBITS, int VBITS>
 __global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __restrict__ v, int n)
 {
-    constexpr int WK = G * KBITS / 32, WV = G * VBITS / 32;
+    constexpr int WK = G * KBITS / 32;
+    constexpr int CPW = 32 / VBITS;  // value codes per 32-bit word
     const int D = p.D;
     const int c = threadIdx.x;
     const size_t bh = blockIdx.x;
     if (c >= D)
-        return;
-    const int ncg = D / G;
-    if (c < ncg) {
-        float x[G];
-        const T* src = v + bh * D + (size_t)c * G;
+        return;  // D is a multiple of 64: whole waves only
+    {
+        const float x = to_f32(v[bh * D + c]);
+        float mn = x, mx = x;
 #pragma unroll
-        for (int j = 0; j < G; ++j)
-            x[j] = to_f32(src[j]);
-        uint32_t w[WV];
-        const uint32_t meta = quantize_pack<VBITS>(x, w);
-        const size_t tc = (bh * p.tcap + n) * ncg + c;
-        uint32_t* dst = p.v_codes + tc * WV;
+        for (int off = 16; off >= 1; off >>= 1) {  // within the 32-lane group
+            mn = fminf(mn, __shfl_xor(mn, off));
+            mx = fmaxf(mx, __shfl_xor(mx, off));
+        }
+        const GroupParams gp = group_params(mn, mx, VBITS);
+        const int j = c % G;
+        uint32_t bits = code_of((double)x, gp, (1 << VBITS) - 1) << ((j * VBITS) % 32);
 #pragma unroll
-        for (int i = 0; i < WV; ++i)
-            dst[i] = w[i];
-        p.v_meta[tc] = meta;
+        for (int off = CPW / 2; off >= 1; off >>= 1)
+            bits |= __shfl_xor(bits, off);
+        const int ncg = D / G, cg = c / G;
+        const size_t tc = (bh * p.tcap + n) * ncg + cg;
+        if (j % CPW == 0)
+            p.v_codes[tc * (G * VBITS / 32) + (j * VBITS) / 32] = bits;
+        if (j == 0)
+            p.v_meta[tc] = gp.meta;
     }
     T* tail = reinterpret_cast<T*>(p.k_tail);
     const int slot = n % G;
