@@ -29,7 +29,46 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, vendor figure
 INFINITY_CACHE = 256 << 20  # bytes
+KERNEL_SOURCES = ["quantized_decode_attention_keys_amd/csrc/kvq_attend_kernel.h",
+                  "quantized_decode_attention_keys_amd/csrc/kvq_internal.h"]
+TRAFFIC_FILE = "profiles/decode_attention_traffic.json"
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config_name: str):
+    """HBM bytes per attention launch from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None when there is none for this
+    workload or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("config") != config_name:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of 1 GiB, three times: the reference
+    whose FETCH_SIZE / WRITE_SIZE readings scale the counters to bytes."""
+    import torch
+    x = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": x.numel() * 4, "copies": 3}))
 
 
 def attend_bytes(cfg, n: int) -> int:
@@ -45,6 +84,15 @@ def attend_bytes(cfg, n: int) -> int:
             + cfg.batch * cfg.q_heads * D * esz + cfg.batch * cfg.q_heads * D * 4)
 
 
+def attend_flops(cfg, n: int) -> int:
+    """The method's fp32 arithmetic per decode call: per cached (key, value)
+    element pair, key dequantize (2) + rotary rotation (3: a pair turns with
+    4 multiplies and 2 adds) + value dequantize (2), and per query head
+    sharing the KV head q.k (2) + p*v (2)."""
+    qpk = cfg.q_heads // cfg.kv_heads
+    return cfg.batch * cfg.kv_heads * n * cfg.head_dim * (7 + 4 * qpk)
+
+
 def prefill_bytes(cfg, n: int) -> int:
     """Quantize-and-pack of n tokens: K and V read once, planes written."""
     G, D = cfg.group, cfg.head_dim
@@ -58,8 +106,12 @@ def prefill_bytes(cfg, n: int) -> int:
 
 
 class HipEvents:
-    """hipEventCreate/Record/ElapsedTime through ctypes: recording costs a
-    few microseconds of host time, so the timed loop stays ahead of the GPU."""
+    """hipEventCreateWithFlags/Record/ElapsedTime through ctypes: recording
+    costs a few microseconds of host time, so the timed loop stays ahead of
+    the GPU.  The events are timing-only (hipEventDisableSystemFence): no
+    system-scope cache writeback/invalidate when they complete."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, count: int):
         import ctypes
@@ -71,8 +123,9 @@ class HipEvents:
         self.ev = []
         for _ in range(count):
             e = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e),
+                                                ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.ev.append(e.value)
 
     def record(self, i: int, stream: int):
@@ -143,7 +196,12 @@ def main():
     ap.add_argument("--config", default="llama2_7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--caches", type=int, default=0, help="rotating caches (0 = auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU component in this build)", file=sys.stderr)
@@ -247,6 +305,8 @@ def main():
     att_avg_s = float(attend_ms.mean()) / 1e3
     bytes_per_launch = total_bytes / len(lengths)
     achieved = bytes_per_launch / att_avg_s / 1e9
+    flops_per_launch = sum(attend_flops(cfg, L) for L in lengths) / len(lengths)
+    achieved_tflops = flops_per_launch / att_avg_s / 1e12
 
     res = {
         "metric": "quantized decode-attention effective KV GB/s (% of HBM peak); tokens/s",
@@ -273,17 +333,21 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(cfg.batch * args.steps / wall, 1),
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "decode attention, HIP events around each kvq_attend_decode call in the timed loop",
+            "bound": "alu",
+            "achieved": round(achieved_tflops, 3),
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(cfg.name),
+            "kernel": "attend_kernel (decode attention); HIP events around each "
+                      "kvq_attend_decode call in the timed loop",
+            "flops_per_launch": int(flops_per_launch),
             "bytes_per_launch": int(bytes_per_launch),
             "avg_launch_us": round(att_avg_s * 1e6, 3),
             "p10_p90_us": [round(float(np.percentile(attend_ms, 10)) * 1e3, 3),
                            round(float(np.percentile(attend_ms, 90)) * 1e3, 3)],
+            "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4)},
         },
         "prefill": {
             "tokens": n - 1,
