@@ -110,39 +110,51 @@ int env_int(const char* name)
     return v ? std::atoi(v) : 0;
 }
 
-// Launch shape of the decode-attention kernel.  Enough waves to fill every
-// compute unit (about 12 resident per CU at the kernel's register use) without
-// splitting a (sequence, KV head) when there are at least as many of those
-// as CUs; otherwise split the token range and merge the partials.
+// Launch shape of the decode-attention kernel.  A compute unit holds about
+// 12 waves of the one-query-head kernel (8 when several query heads share a
+// KV head: more registers).  Best measured: blocks of that full size, with
+// splits chosen so that blocks = k * CUs for a small k (every CU gets the
+// same whole number of blocks); without such a fit, 4-wave blocks and enough
+// splits for about three blocks per CU, which keeps the last round short.
 void attend_shape(const kvq* h, int n, int* splits_out, int* waves_out)
 {
-    constexpr int kWavesPerCu = 12;
     const int units = h->cfg.batch * h->cfg.kv_heads;
     const int cus = h->cus > 0 ? h->cus : 256;
     const int full_groups = n / h->cfg.group;
     const int groups_per_step = 64 / (h->cfg.head_dim / 2);
-    int splits, waves;
-    if (units >= cus) {
-        splits = 1;
-        waves = kWavesPerCu * cus / units;
-    } else {
-        splits = (2 * cus + units - 1) / units;
-        waves = kWavesPerCu / 2;
+    const int qpk = h->cfg.q_heads / h->cfg.kv_heads;
+    const int wpc = qpk == 1 ? 12 : 8;
+    const int cap = full_groups > 0 ? full_groups : 1;
+    const int max_splits = h->layout.max_splits < cap ? h->layout.max_splits : cap;
+    int splits = 0, waves = 0;
+    for (int k = 1; k <= 4 && splits == 0; ++k) {
+        if ((long long)k * cus % units != 0)
+            continue;
+        const long long sp = (long long)k * cus / units;
+        if (sp >= 1 && sp <= max_splits) {
+            splits = (int)sp;
+            waves = wpc;
+        }
+    }
+    if (splits == 0) {
+        waves = 4;
+        splits = (int)(((long long)(wpc / waves) * cus + units - 1) / units);
+        if (splits > max_splits)
+            splits = max_splits;
+        if (splits < 1)
+            splits = 1;
     }
     if (h->force_splits > 0)
-        splits = h->force_splits;
-    if (splits > h->layout.max_splits)
-        splits = h->layout.max_splits;
-    if (splits > full_groups)
-        splits = full_groups > 0 ? full_groups : 1;
+        splits = h->force_splits < max_splits ? h->force_splits : max_splits;
+    // waves beyond the groups of a block would idle
     const int per_block = (full_groups + splits - 1) / splits;
     const int useful = (per_block + groups_per_step - 1) / groups_per_step;
     if (waves > useful)
         waves = useful;
     if (h->force_waves > 0)
         waves = h->force_waves;
-    if (waves > 12)
-        waves = 12;  // the kernel's block limit
+    if (waves > wpc)
+        waves = wpc;
     if (waves < 1)
         waves = 1;
     *splits_out = splits;
