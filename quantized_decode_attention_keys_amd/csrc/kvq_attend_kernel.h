@@ -51,11 +51,7 @@ namespace {
 
 constexpr int G = kGroup;
 constexpr float kLog2e = 1.4426950408889634f;
-// Block size limit: 12 waves (up to 168 VGPRs per lane) with one query head
-// per KV head, 8 waves (up to 256 VGPRs) when several query heads share one.
-constexpr int kMaxWaves = 12;
-template <int QPK>
-constexpr int max_waves() { return QPK == 1 ? 12 : 8; }
+constexpr int kMaxWaves = 16;  // max_block_waves over all variants
 
 __device__ __forceinline__ float h2f(uint32_t bits16)
 {
@@ -126,25 +122,61 @@ constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane k <-> 7-k within each 8
 constexpr int kDppMirror = 0x140;     // lane k <-> 15-k within each 16
 
-// Maximum over the wave: four DPP steps inside each 16-lane row, then two
-// cross-row exchanges.
+// Cross-row exchanges on the VALU (no LDS round trip).  With both operands
+// equal to v, the 16-lane swap returns {rows (0,0,2,2) of v, rows (1,1,3,3)}
+// and the 32-lane swap {lanes 0..31 of v twice, lanes 32..63 twice}.
+struct Pair {
+    float a, b;
+};
+__device__ __forceinline__ Pair swap16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ Pair swap32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// v[l] + v[l ^ 32], the same bits in both lanes.
+__device__ __forceinline__ float half_sum(float v)
+{
+    const Pair r = swap32(v);
+    return r.a + r.b;
+}
+
+// Maximum over the wave: four DPP steps inside each 16-lane row, then the
+// cross-row swaps.  HALVES_EQUAL: lanes l and l + 32 hold the same value, so
+// the 32-lane step is skipped.
+template <bool HALVES_EQUAL>
 __device__ __forceinline__ float wave_max(float v)
 {
     v = fmaxf(v, dpp<kDppXor1>(v));
     v = fmaxf(v, dpp<kDppXor2>(v));
     v = fmaxf(v, dpp<kDppHalfMirror>(v));
     v = fmaxf(v, dpp<kDppMirror>(v));
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
+    const Pair r = swap16(v);
+    v = fmaxf(r.a, r.b);
+    if (!HALVES_EQUAL) {
+        const Pair t = swap32(v);
+        v = fmaxf(t.a, t.b);
+    }
     return v;
 }
 
+// Sum over the wave (the same value in every lane, up to the order of the
+// additions): as wave_max.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off);
-    return v;
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    const Pair r = swap16(v);
+    v = r.a + r.b;
+    const Pair t = swap32(v);
+    return t.a + t.b;
 }
 
 template <int D, int KB, int VB, int QPK>
@@ -161,16 +193,26 @@ struct Shape {
     static constexpr int NC = 32 / VB;         // channels per value word
     static constexpr int RED_STRIDE = 33;      // floats per lane row of the reduce buffer
     static_assert(64 % WPT == 0 && TPW % TS == 0, "value lane mapping");
+    // Value lane mapping.  Token pairs (one query head, head_dim 128): lane =
+    // (row r = lane / 16, column c = lane % 16) takes tokens c and c + 16 of
+    // the step and all 32 channels of value group r, so the weights it needs
+    // sit in its own 16-lane row pair and one swap fetches both.  Otherwise
+    // lane = (code word, token slot) as described at the top.
+    static constexpr bool PAIRS = (QPK == 1 && NP == 64);
+    static_assert(!PAIRS || NCG == 4, "one value group per 16-lane row");
+    static constexpr int NVW = PAIRS ? 2 * WV : VTOK;   // value code words per lane per step
+    static constexpr int NVM = PAIRS ? 2 : VTOK;        // value meta words per lane per step
+    static constexpr int NCL = PAIRS ? G : NC;          // value channels per lane
 };
 
 // Everything one wave step reads from memory, loaded one step ahead.
-template <int WK, int VTOK>
+template <int WK, int NVW, int NVM>
 struct StepData {
     uint32_t kw[2 * WK];   // key codes of the lane's two channels
     uint2 km;              // their (step, zero) meta words
     float2 rg;             // e^{i g G theta_i}
-    uint32_t vw[VTOK];     // value code word per value token
-    uint32_t vm[VTOK];     // value meta word per value token
+    uint32_t vw[NVW];      // value code words of the lane's value tokens
+    uint32_t vm[NVM];      // their value meta words
 };
 
 // Per-wave online-softmax state and value accumulators.
@@ -192,10 +234,48 @@ struct HeadPlanes {
     const uint32_t* vm;   // [tcap][NCG]
 };
 
+// Value words of the lane's tokens among t0 .. t0 + TPW - 1 (indexes
+// clamped to t_last, a token the cache holds).
 template <int D, int KB, int VB, int QPK>
-__device__ __forceinline__ void load_step(const HeadPlanes& hp, const float2* __restrict__ rope_group,
-                                          int lane, int gb, int g1,
-                                          StepData<KB, Shape<D, KB, VB, QPK>::VTOK>& sd)
+__device__ __forceinline__ void load_values(const HeadPlanes& hp, int lane, int t0, int t_last,
+                                            uint32_t (&vw)[Shape<D, KB, VB, QPK>::NVW],
+                                            uint32_t (&vm)[Shape<D, KB, VB, QPK>::NVM])
+{
+    using S = Shape<D, KB, VB, QPK>;
+    if constexpr (S::PAIRS) {
+        const unsigned r = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const unsigned t = (unsigned)min(t0 + (int)c + 16 * k, t_last);
+            const uint32_t* src = hp.vc + t * S::WPT + r * S::WV;
+            if constexpr (S::WV == 2) {
+                const uint2 w = *reinterpret_cast<const uint2*>(src);
+                vw[2 * k] = w.x;
+                vw[2 * k + 1] = w.y;
+            } else {
+                uint32_t w[S::WV];
+                load_words<S::WV>(src, w);
+#pragma unroll
+                for (int u = 0; u < S::WV; ++u)
+                    vw[k * S::WV + u] = w[u];
+            }
+            vm[k] = hp.vm[t * S::NCG + r];
+        }
+    } else {
+        const unsigned w = lane % S::WPT, vslot = lane / S::WPT, vcg = w / S::WV;
+#pragma unroll
+        for (int k = 0; k < S::VTOK; ++k) {
+            const unsigned t = (unsigned)min(t0 + (int)vslot + k * S::TS, t_last);
+            vw[k] = hp.vc[t * S::WPT + w];
+            vm[k] = hp.vm[t * S::NCG + vcg];
+        }
+    }
+}
+
+template <int D, int KB, int VB, int QPK>
+__device__ __forceinline__ void load_step(
+    const HeadPlanes& hp, const float2* __restrict__ rope_group, int lane, int gb, int g1,
+    StepData<KB, Shape<D, KB, VB, QPK>::NVW, Shape<D, KB, VB, QPK>::NVM>& sd)
 {
     using S = Shape<D, KB, VB, QPK>;
     const unsigned i = lane % S::NP, gsub = lane / S::NP;
@@ -204,14 +284,7 @@ __device__ __forceinline__ void load_step(const HeadPlanes& hp, const float2* __
     load_words<2 * S::WK>(hp.kc + gc * S::WK, sd.kw);
     sd.km = *reinterpret_cast<const uint2*>(hp.km + gc);
     sd.rg = rope_group[g * S::NP + i];
-    const unsigned vw = lane % S::WPT, vslot = lane / S::WPT, vcg = vw / S::WV;
-    const int t_last = g1 * G - 1;
-#pragma unroll
-    for (int k = 0; k < S::VTOK; ++k) {
-        const unsigned t = (unsigned)min(gb * G + (int)vslot + k * S::TS, t_last);
-        sd.vw[k] = hp.vc[t * S::WPT + vw];
-        sd.vm[k] = hp.vm[t * S::NCG + vcg];
-    }
+    load_values<D, KB, VB, QPK>(hp, lane, gb * G, g1 * G - 1, sd.vw, sd.vm);
 }
 
 // Softmax update for one wave step and accumulation of its value tokens.
@@ -222,7 +295,7 @@ template <int D, int KB, int VB, int QPK>
 __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
                                                const float (&s)[QPK], const uint32_t* vwords,
                                                const uint32_t* vmetas,
-                                               WaveState<QPK, 32 / VB>& st)
+                                               WaveState<QPK, Shape<D, KB, VB, QPK>::NCL>& st)
 {
     using S = Shape<D, KB, VB, QPK>;
     using C = Codec<VB>;
@@ -233,7 +306,7 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
 #pragma unroll
     for (int h = 0; h < QPK; ++h) {
         const float sv = own_valid ? s[h] : -INFINITY;
-        const float m_new = fmaxf(st.m[h], wave_max(sv));
+        const float m_new = fmaxf(st.m[h], wave_max<S::NP == 64>(sv));
         const float alpha = exp2f(st.m[h] - m_new);  // 0 on the first step
         const float pl = own_valid ? exp2f(sv - m_new) : 0.f;
         st.l[h] = st.l[h] * alpha + (counts ? pl : 0.f);
@@ -242,9 +315,33 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
         if (alpha != 1.f) {  // uniform across the wave
             st.z[h] *= alpha;
 #pragma unroll
-            for (int c = 0; c < S::NC; ++c)
+            for (int c = 0; c < S::NCL; ++c)
                 st.o[h][c] *= alpha;
         }
+    }
+    if constexpr (S::PAIRS) {
+        // weights of tokens c and c + 16: lanes of rows 0 and 2 hold token
+        // c's, rows 1 and 3 token c + 16's
+        const Pair pp = swap16(pw[0]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float pt = k ? pp.b : pp.a;  // 0 for absent tokens
+            const float ps = pt * lo_h(vmetas[k]);
+            st.z[0] = fmaf(pt, hi_h(vmetas[k]), st.z[0]);
+#pragma unroll
+            for (int u = 0; u < S::WV; ++u) {
+                const uint32_t word = vwords[k * S::WV + u];
+                const uint32_t wsh = word >> C::SHIFT;
+#pragma unroll
+                for (int f = 0; f < C::TPH; ++f) {
+                    const uint32_t m = C::field(word, wsh, f);
+                    st.o[0][u * S::NC + f] = fmaf(ps, lo_h(m), st.o[0][u * S::NC + f]);
+                    st.o[0][u * S::NC + C::TPH + f] =
+                        fmaf(ps, hi_h(m), st.o[0][u * S::NC + C::TPH + f]);
+                }
+            }
+        }
+        return;
     }
     const int vslot = lane / S::WPT;
 #pragma unroll
@@ -268,7 +365,7 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
 }
 
 template <int D, int KB, int VB, int QPK>
-__global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p, const void* __restrict__ q,
+__global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kernel(Planes p, const void* __restrict__ q,
                                                                 float* __restrict__ out, int n,
                                                                 int splits)
 {
@@ -280,7 +377,8 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
     extern __shared__ float smem[];  // [nwaves][64][RS] reduce buffers, reused for the merge
 
     const int nwaves = blockDim.x >> 6;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
     const int i = lane % NP, gsub = lane / NP;
     const int split = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -289,6 +387,19 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
     const int g0 = (int)((long long)split * ngq / splits);
     const int g1 = (int)((long long)(split + 1) * ngq / splits);
     const bool do_tail = (split == splits - 1) && cnt_tail > 0;
+
+    // The first step's words go out before anything else: their HBM latency
+    // overlaps the query rotation and the twiddle staging.
+    HeadPlanes hp;
+    hp.kc = p.k_codes + bh * (size_t)p.gcap * D * S::WK;
+    hp.km = p.k_meta + bh * (size_t)p.gcap * D;
+    hp.vc = p.v_codes + bh * (size_t)p.tcap * S::WPT;
+    hp.vm = p.v_meta + bh * (size_t)p.tcap * S::NCG;
+    const int stride = nwaves * S::GPW;
+    StepData<KB, S::NVW, S::NVM> cur, nxt;
+    int gb = g0 + wave * S::GPW;
+    if (gb < g1)
+        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
 
     // conj(q') * log2(e)/sqrt(D) for this lane's pair, q' = q rotated to n-1
     float2 qc[QPK];
@@ -304,54 +415,63 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
             qc[h] = make_float2(qq.x * scale, -qq.y * scale);
         }
     }
-    // per-token twiddles e^{i j theta_i}, pre-scaled by 2^(24 - pos) of the
-    // field that holds token j (j = word * 2*TPH + half * TPH + field)
-    float2 tw[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const float2 t = p.rope_offset[j * NP + i];
-        const float sc = (float)(1 << (24 - KC::pos(j % KC::TPH)));
-        tw[j] = make_float2(t.x * sc, -t.y * sc);
+    // Per-token twiddles e^{i j theta_i}, pre-scaled by 2^(24 - pos) of the
+    // field that holds token j (j = word * 2*TPH + half * TPH + field), staged
+    // once per block: entry (j/2, pair) holds tokens j and j+1 as
+    // (T.x, -T.y) pairs.  A separate array from the reduce buffers, so its
+    // reads are never ordered after their writes.
+    __shared__ float4 twl[G / 2 * 64];
+    for (int idx = threadIdx.x; idx < G / 2 * NP; idx += blockDim.x) {
+        const int jp = idx / NP, ii = idx % NP;
+        const float2 t0 = p.rope_offset[(2 * jp) * NP + ii];
+        const float2 t1 = p.rope_offset[(2 * jp + 1) * NP + ii];
+        const float sc0 = (float)(1 << (24 - KC::pos((2 * jp) % KC::TPH)));
+        const float sc1 = (float)(1 << (24 - KC::pos((2 * jp + 1) % KC::TPH)));
+        twl[idx] = make_float4(t0.x * sc0, -t0.y * sc0, t1.x * sc1, -t1.y * sc1);
     }
+    __syncthreads();
+    // Where the registers allow it (twiddles_in_lds false) the wave copies its
+    // 32 twiddles into registers once; otherwise it reads them from LDS where
+    // they are used, and tw_base is re-made opaque every step so the compiler
+    // cannot hoist those reads out of the loop.
+    constexpr bool TWL = twiddles_in_lds(QPK, KB, VB);
+    int tw_base = i;
+    float2 twr[TWL ? 1 : G];
+    if constexpr (!TWL) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float4 t = twl[(j >> 1) * NP + i];
+            twr[j] = (j & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
+        }
+    }
+    auto twiddle = [&](int j) {
+        if constexpr (TWL) {
+            const float4 t = twl[(j >> 1) * NP + tw_base];
+            return (j & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
+        } else {
+            return twr[j];
+        }
+    };
 
-    WaveState<QPK, S::NC> st;
+    WaveState<QPK, S::NCL> st;
 #pragma unroll
     for (int h = 0; h < QPK; ++h) {
         st.m[h] = -INFINITY;
         st.l[h] = 0.f;
         st.z[h] = 0.f;
 #pragma unroll
-        for (int c = 0; c < S::NC; ++c)
+        for (int c = 0; c < S::NCL; ++c)
             st.o[h][c] = 0.f;
     }
     float* red = smem + wave * 64 * RS;
     const int red_half = lane & ~31, red_col = lane & 31;
 
-    HeadPlanes hp;
-    hp.kc = p.k_codes + bh * (size_t)p.gcap * D * S::WK;
-    hp.km = p.k_meta + bh * (size_t)p.gcap * D;
-    hp.vc = p.v_codes + bh * (size_t)p.tcap * S::WPT;
-    hp.vm = p.v_meta + bh * (size_t)p.tcap * S::NCG;
-    const int stride = nwaves * S::GPW;
-    StepData<KB, S::VTOK> cur, nxt;
-    int gb = g0 + wave * S::GPW;
-    if (gb < g1)
-        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
-
     if (do_tail && wave == nwaves - 1) {
         // The tail (cnt_tail < G unquantized keys, slot j = token tq + j) is
         // scored like one more group by the wave with the fewest groups:
         // lane = channel pair, the tail tokens across the lane's registers.
-        uint32_t vw[S::VTOK], vm[S::VTOK];
-        {
-            const int vwi = lane % S::WPT, vslot = lane / S::WPT, vcg = vwi / S::WV;
-#pragma unroll
-            for (int k = 0; k < S::VTOK; ++k) {
-                const unsigned t = (unsigned)min(tq + vslot + k * S::TS, n - 1);
-                vw[k] = hp.vc[t * S::WPT + vwi];
-                vm[k] = hp.vm[t * S::NCG + vcg];
-            }
-        }
+        uint32_t vw[S::NVW], vm[S::NVM];
+        load_values<D, KB, VB, QPK>(hp, lane, tq, n - 1, vw, vm);
         float tx[G], ty[G];
         const size_t trow = (bh * G) * D + 2 * i;  // element index of (slot 0, channel 2i)
         if (p.dtype == 0) {
@@ -379,11 +499,12 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
             const float2 Q = cmul(qc[h], rg);
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                // Re[T_j Q (x + iy)]; tw[j] carries (T.x, -T.y) * 2^(24-pos)
+                // Re[T_j Q (x + iy)]; the twiddle carries (T.x, -T.y) * 2^(24-pos)
                 const float vr = Q.x * tx[j] - Q.y * ty[j];
                 const float vi = Q.x * ty[j] + Q.y * tx[j];
                 const float unscale = 1.0f / (float)(1 << (24 - KC::pos(j % KC::TPH)));
-                red[lane * RS + j] = fmaf(tw[j].x, vr, tw[j].y * vi) * unscale;
+                const float2 tw = twiddle(j);
+                red[lane * RS + j] = fmaf(tw.x, vr, tw.y * vi) * unscale;
             }
             float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -391,13 +512,35 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
                 a4[m & 3] += red[(red_half + m) * RS + red_col];
             float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
             if (NP == 64)
-                acc += __shfl_xor(acc, 32);
+                acc = half_sum(acc);
             s[h] = acc;
         }
         softmax_values<D, KB, VB, QPK>(lane, tq, n, s, vw, vm, st);
     }
 
+    // Waves of a SIMD otherwise run oldest-first, so the oldest finishes its
+    // share long before the youngest, which then runs alone at a fraction of
+    // the SIMD's issue rate.  Each wave lowers its priority by one level per
+    // quarter of its share done, so the waves of a SIMD finish together.
+    const int my_steps = gb < g1 ? (g1 - 1 - gb) / stride + 1 : 0;
+    // step d is in quarter floor(4 d / my_steps): d >= ceil(k my_steps / 4)
+    const int q1 = (my_steps + 3) / 4, q2 = (2 * my_steps + 3) / 4, q3 = (3 * my_steps + 3) / 4;
+    int done = 0;
     for (; gb < g1; gb += stride) {
+        if constexpr (TWL)
+            asm volatile("" : "+v"(tw_base));
+        {
+            const int quarter = (done >= q1) + (done >= q2) + (done >= q3);
+            ++done;
+            if (quarter == 0)
+                __builtin_amdgcn_s_setprio(3);
+            else if (quarter == 1)
+                __builtin_amdgcn_s_setprio(2);
+            else if (quarter == 2)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
+        }
         // unconditional (clamped) prefetch: straight-line code lets the
         // compiler wait only for the current step's loads
         load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, min(gb + stride, g1 - 1), g1, nxt);
@@ -432,7 +575,8 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
                         const float c1 = half ? hi_h(m1) : lo_h(m1);
                         const float X = fmaf(bb, c1, fmaf(a, c0, Ps[sidx]));
                         const float Y = fmaf(e, c1, fmaf(d, c0, Rs[sidx]));
-                        red[lane * RS + j] = fmaf(tw[j].x, X, tw[j].y * Y);
+                        const float2 tw = twiddle(j);
+                        red[lane * RS + j] = fmaf(tw.x, X, tw.y * Y);
                     }
                 }
             }
@@ -442,19 +586,41 @@ __global__ __launch_bounds__(64 * max_waves<QPK>()) void attend_kernel(Planes p,
                 a4[m & 3] += red[(red_half + m) * RS + red_col];
             float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
             if (NP == 64)
-                acc += __shfl_xor(acc, 32);
+                acc = half_sum(acc);
             s[h] = acc;
         }
         softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, cur.vw, cur.vm, st);
         cur = nxt;
     }
 
+    __builtin_amdgcn_s_setprio(0);
+
     // ---- merge the waves of this block
     __syncthreads();  // every wave is done with its reduce buffer
     float* sm = smem;                           // [nwaves][QPK]
     float* sl = smem + kMaxWaves * QPK;         // [nwaves][QPK]
     float* so = smem + 2 * kMaxWaves * QPK;     // [nwaves][QPK][D]
-    {
+    if constexpr (S::PAIRS) {
+        // lane (r, c) holds channel group r over its tokens: sum the 16
+        // lanes of row r per channel
+        const float L = wave_sum(st.l[0]);
+        const int r = lane >> 4;
+#pragma unroll
+        for (int c = 0; c < G; ++c) {
+            const float sc = (float)(1 << (24 - VC::pos(c % VC::TPH)));
+            float x = fmaf(st.o[0][c], sc, st.z[0]);
+            x += dpp<kDppXor1>(x);
+            x += dpp<kDppXor2>(x);
+            x += dpp<kDppHalfMirror>(x);
+            x += dpp<kDppMirror>(x);
+            if ((lane & 15) == 0)
+                so[wave * D + r * G + c] = x;
+        }
+        if (lane == 0) {
+            sm[wave] = st.m[0];
+            sl[wave] = L;
+        }
+    } else {
         const int vw = lane % S::WPT, vslot = lane / S::WPT;
 #pragma unroll
         for (int h = 0; h < QPK; ++h) {
@@ -552,7 +718,7 @@ void launch(const Planes& p, const void* q, float* out, int n, int splits, int n
             hipStream_t stream)
 {
     dim3 grid(splits, p.nb * p.hkv);
-    nwaves = nwaves < max_waves<QPK>() ? nwaves : max_waves<QPK>();
+    nwaves = nwaves < max_block_waves(QPK, KB, VB) ? nwaves : max_block_waves(QPK, KB, VB);
     attend_kernel<D, KB, VB, QPK><<<grid, 64 * nwaves, attend_lds_bytes<D, KB, VB, QPK>(nwaves),
                                     stream>>>(p, q, out, n, splits);
     if (splits > 1)
