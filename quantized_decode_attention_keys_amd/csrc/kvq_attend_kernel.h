@@ -234,20 +234,27 @@ struct HeadPlanes {
     const uint32_t* vm;   // [tcap][NCG]
 };
 
-// Value words of the lane's tokens among t0 .. t0 + TPW - 1 (indexes
-// clamped to t_last, a token the cache holds).
-template <int D, int KB, int VB, int QPK>
+// Value words of the lane's tokens among t0 .. t0 + TPW - 1.  Addresses are
+// a wave-uniform base (scalar registers) plus a 32-bit lane offset.  CLAMP:
+// some of those tokens may lie past t_last, the last token the cache holds;
+// their indexes are clamped to it (the words are loaded but weigh 0).
+template <int D, int KB, int VB, int QPK, bool CLAMP>
 __device__ __forceinline__ void load_values(const HeadPlanes& hp, int lane, int t0, int t_last,
                                             uint32_t (&vw)[Shape<D, KB, VB, QPK>::NVW],
                                             uint32_t (&vm)[Shape<D, KB, VB, QPK>::NVM])
 {
     using S = Shape<D, KB, VB, QPK>;
+    const uint32_t* vc0 = hp.vc + (size_t)t0 * S::WPT;
+    const uint32_t* vm0 = hp.vm + (size_t)t0 * S::NCG;
+    auto slot = [&](unsigned tt) {
+        return CLAMP ? (unsigned)(min(t0 + (int)tt, t_last) - t0) : tt;
+    };
     if constexpr (S::PAIRS) {
         const unsigned r = lane >> 4, c = lane & 15;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const unsigned t = (unsigned)min(t0 + (int)c + 16 * k, t_last);
-            const uint32_t* src = hp.vc + t * S::WPT + r * S::WV;
+            const unsigned tt = slot(c + 16 * k);
+            const uint32_t* src = vc0 + tt * S::WPT + r * S::WV;
             if constexpr (S::WV == 2) {
                 const uint2 w = *reinterpret_cast<const uint2*>(src);
                 vw[2 * k] = w.x;
@@ -259,19 +266,21 @@ __device__ __forceinline__ void load_values(const HeadPlanes& hp, int lane, int 
                 for (int u = 0; u < S::WV; ++u)
                     vw[k * S::WV + u] = w[u];
             }
-            vm[k] = hp.vm[t * S::NCG + r];
+            vm[k] = vm0[tt * S::NCG + r];
         }
     } else {
         const unsigned w = lane % S::WPT, vslot = lane / S::WPT, vcg = w / S::WV;
 #pragma unroll
         for (int k = 0; k < S::VTOK; ++k) {
-            const unsigned t = (unsigned)min(t0 + (int)vslot + k * S::TS, t_last);
-            vw[k] = hp.vc[t * S::WPT + w];
-            vm[k] = hp.vm[t * S::NCG + vcg];
+            const unsigned tt = slot(vslot + k * S::TS);
+            vw[k] = vc0[tt * S::WPT + w];
+            vm[k] = vm0[tt * S::NCG + vcg];
         }
     }
 }
 
+// Key words, metadata and group rotation of key group gb (and gb + 1 for
+// head_dim 64) plus the value words of its tokens; gb <= g1 - 1.
 template <int D, int KB, int VB, int QPK>
 __device__ __forceinline__ void load_step(
     const HeadPlanes& hp, const float2* __restrict__ rope_group, int lane, int gb, int g1,
@@ -279,12 +288,13 @@ __device__ __forceinline__ void load_step(
 {
     using S = Shape<D, KB, VB, QPK>;
     const unsigned i = lane % S::NP, gsub = lane / S::NP;
-    const unsigned g = (unsigned)min(gb + (int)gsub, g1 - 1);  // clamped: always a real group
-    const unsigned gc = g * D + 2 * i;
-    load_words<2 * S::WK>(hp.kc + gc * S::WK, sd.kw);
-    sd.km = *reinterpret_cast<const uint2*>(hp.km + gc);
-    sd.rg = rope_group[g * S::NP + i];
-    load_values<D, KB, VB, QPK>(hp, lane, gb * G, g1 * G - 1, sd.vw, sd.vm);
+    // head_dim 64: the second group of the step, if any, else the first again
+    const unsigned gl = (S::GPW > 1 && gsub != 0 && gb + 1 < g1) ? 1u : 0u;
+    const unsigned ci = gl * D + 2 * i;
+    load_words<2 * S::WK>(hp.kc + (size_t)gb * (D * S::WK) + ci * S::WK, sd.kw);
+    sd.km = *reinterpret_cast<const uint2*>(hp.km + (size_t)gb * D + ci);
+    sd.rg = rope_group[(size_t)gb * S::NP + gl * S::NP + i];
+    load_values<D, KB, VB, QPK, (S::GPW > 1)>(hp, lane, gb * G, g1 * G - 1, sd.vw, sd.vm);
 }
 
 // Softmax update for one wave step and accumulation of its value tokens.
@@ -307,8 +317,10 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
     for (int h = 0; h < QPK; ++h) {
         const float sv = own_valid ? s[h] : -INFINITY;
         const float m_new = fmaxf(st.m[h], wave_max<S::NP == 64>(sv));
-        const float alpha = exp2f(st.m[h] - m_new);  // 0 on the first step
-        const float pl = own_valid ? exp2f(sv - m_new) : 0.f;
+        // arguments <= 0; v_exp_f32 returns 0 for -inf and for results below
+        // the fp32 normal range, which weigh nothing at this tolerance
+        const float alpha = __builtin_amdgcn_exp2f(st.m[h] - m_new);  // 0 on the first step
+        const float pl = own_valid ? __builtin_amdgcn_exp2f(sv - m_new) : 0.f;
         st.l[h] = st.l[h] * alpha + (counts ? pl : 0.f);
         st.m[h] = m_new;
         pw[h] = pl;
@@ -471,7 +483,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
         // scored like one more group by the wave with the fewest groups:
         // lane = channel pair, the tail tokens across the lane's registers.
         uint32_t vw[S::NVW], vm[S::NVM];
-        load_values<D, KB, VB, QPK>(hp, lane, tq, n - 1, vw, vm);
+        load_values<D, KB, VB, QPK, true>(hp, lane, tq, n - 1, vw, vm);
         float tx[G], ty[G];
         const size_t trow = (bh * G) * D + 2 * i;  // element index of (slot 0, channel 2i)
         if (p.dtype == 0) {
@@ -526,7 +538,10 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
     // step d is in quarter floor(4 d / my_steps): d >= ceil(k my_steps / 4)
     const int q1 = (my_steps + 3) / 4, q2 = (2 * my_steps + 3) / 4, q3 = (3 * my_steps + 3) / 4;
     int done = 0;
-    for (; gb < g1; gb += stride) {
+    using Step = StepData<KB, S::NVW, S::NVM>;
+    // One wave step on the words in `use` while the next step's words load
+    // into `fill`; the loop below alternates the two buffers.
+    auto step = [&](Step& use, Step& fill) __attribute__((always_inline)) {
         if constexpr (TWL)
             asm volatile("" : "+v"(tw_base));
         {
@@ -543,13 +558,13 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
         }
         // unconditional (clamped) prefetch: straight-line code lets the
         // compiler wait only for the current step's loads
-        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, min(gb + stride, g1 - 1), g1, nxt);
-        const float s0 = h2f(cur.km.x), z0 = h2f(cur.km.x >> 16);
-        const float s1 = h2f(cur.km.y), z1 = h2f(cur.km.y >> 16);
+        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, min(gb + stride, g1 - 1), g1, fill);
+        const float s0 = h2f(use.km.x), z0 = h2f(use.km.x >> 16);
+        const float s1 = h2f(use.km.y), z1 = h2f(use.km.y >> 16);
         float s[QPK];
 #pragma unroll
         for (int h = 0; h < QPK; ++h) {
-            const float2 Q = cmul(qc[h], cur.rg);
+            const float2 Q = cmul(qc[h], use.rg);
             // X = P + a c0 + bb c1 = Re[Q (x+iy)],  Y = R + d c0 + e c1 = Im[Q (x+iy)]
             const float P = Q.x * z0 - Q.y * z1, a = Q.x * s0, bb = -Q.y * s1;
             const float R = Q.y * z0 + Q.x * z1, d = Q.y * s0, e = Q.x * s1;
@@ -562,7 +577,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
             }
 #pragma unroll
             for (int w = 0; w < S::WK; ++w) {
-                const uint32_t w0 = cur.kw[w], w1 = cur.kw[S::WK + w];
+                const uint32_t w0 = use.kw[w], w1 = use.kw[S::WK + w];
                 const uint32_t w0s = w0 >> KC::SHIFT, w1s = w1 >> KC::SHIFT;
 #pragma unroll
                 for (int f = 0; f < KC::TPH; ++f) {
@@ -589,8 +604,14 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
                 acc = half_sum(acc);
             s[h] = acc;
         }
-        softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, cur.vw, cur.vm, st);
-        cur = nxt;
+        softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, use.vw, use.vm, st);
+        gb += stride;
+    };
+    while (gb < g1) {
+        step(cur, nxt);
+        if (gb >= g1)
+            break;
+        step(nxt, cur);
     }
 
     __builtin_amdgcn_s_setprio(0);

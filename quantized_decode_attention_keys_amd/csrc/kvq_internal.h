@@ -15,7 +15,7 @@ constexpr int kGroup = 32;  // G: tokens per key group, channels per value group
 // head per KV head with 4- or 8-bit values or 8-bit keys.
 constexpr bool twiddles_in_lds(int qpk, int kbits, int vbits)
 {
-    return qpk == 1 && (vbits >= 4 || kbits >= 8);
+    return qpk == 1;
 }
 
 // Largest attention block in waves: 16 (up to 128 VGPRs per lane) with the
