@@ -377,7 +377,7 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
 }
 
 template <int D, int KB, int VB, int QPK>
-__global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kernel(Planes p, const void* __restrict__ q,
+__global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Planes p, const void* __restrict__ q,
                                                                 float* __restrict__ out, int n,
                                                                 int splits)
 {
@@ -442,27 +442,13 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
         twl[idx] = make_float4(t0.x * sc0, -t0.y * sc0, t1.x * sc1, -t1.y * sc1);
     }
     __syncthreads();
-    // Where the registers allow it (twiddles_in_lds false) the wave copies its
-    // 32 twiddles into registers once; otherwise it reads them from LDS where
-    // they are used, and tw_base is re-made opaque every step so the compiler
-    // cannot hoist those reads out of the loop.
-    constexpr bool TWL = twiddles_in_lds(QPK, KB, VB);
+    // Every wave reads the twiddles from LDS where it uses them: tw_base is
+    // re-made opaque every step, so the compiler cannot hoist those reads
+    // into 64 registers held for the whole loop.
     int tw_base = i;
-    float2 twr[TWL ? 1 : G];
-    if constexpr (!TWL) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float4 t = twl[(j >> 1) * NP + i];
-            twr[j] = (j & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
-        }
-    }
     auto twiddle = [&](int j) {
-        if constexpr (TWL) {
-            const float4 t = twl[(j >> 1) * NP + tw_base];
-            return (j & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
-        } else {
-            return twr[j];
-        }
+        const float4 t = twl[(j >> 1) * NP + tw_base];
+        return (j & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
     };
 
     WaveState<QPK, S::NCL> st;
@@ -542,8 +528,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
     // One wave step on the words in `use` while the next step's words load
     // into `fill`; the loop below alternates the two buffers.
     auto step = [&](Step& use, Step& fill) __attribute__((always_inline)) {
-        if constexpr (TWL)
-            asm volatile("" : "+v"(tw_base));
+        asm volatile("" : "+v"(tw_base));
         {
             const int quarter = (done >= q1) + (done >= q2) + (done >= q3);
             ++done;
@@ -562,19 +547,62 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
         const float s0 = h2f(use.km.x), z0 = h2f(use.km.x >> 16);
         const float s1 = h2f(use.km.y), z1 = h2f(use.km.y >> 16);
         float s[QPK];
-#pragma unroll
-        for (int h = 0; h < QPK; ++h) {
-            const float2 Q = cmul(qc[h], use.rg);
-            // X = P + a c0 + bb c1 = Re[Q (x+iy)],  Y = R + d c0 + e c1 = Im[Q (x+iy)]
-            const float P = Q.x * z0 - Q.y * z1, a = Q.x * s0, bb = -Q.y * s1;
-            const float R = Q.y * z0 + Q.x * z1, d = Q.y * s0, e = Q.x * s1;
-            float Ps[KC::NSCALE], Rs[KC::NSCALE];
+        if constexpr (QPK == 1) {
+    #pragma unroll
+            for (int h = 0; h < QPK; ++h) {
+                const float2 Q = cmul(qc[h], use.rg);
+                // X = P + a c0 + bb c1 = Re[Q (x+iy)],  Y = R + d c0 + e c1 = Im[Q (x+iy)]
+                const float P = Q.x * z0 - Q.y * z1, a = Q.x * s0, bb = -Q.y * s1;
+                const float R = Q.y * z0 + Q.x * z1, d = Q.y * s0, e = Q.x * s1;
+                float Ps[KC::NSCALE], Rs[KC::NSCALE];
+    #pragma unroll
+                for (int k = 0; k < KC::NSCALE; ++k) {
+                    const float sc = 1.0f / (float)(1 << (24 - k * KB));
+                    Ps[k] = P * sc;
+                    Rs[k] = R * sc;
+                }
+    #pragma unroll
+                for (int w = 0; w < S::WK; ++w) {
+                    const uint32_t w0 = use.kw[w], w1 = use.kw[S::WK + w];
+                    const uint32_t w0s = w0 >> KC::SHIFT, w1s = w1 >> KC::SHIFT;
+    #pragma unroll
+                    for (int f = 0; f < KC::TPH; ++f) {
+                        const uint32_t m0 = KC::field(w0, w0s, f), m1 = KC::field(w1, w1s, f);
+                        const int sidx = KC::pos(f) / KB;
+    #pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const int j = w * 2 * KC::TPH + half * KC::TPH + f;
+                            const float c0 = half ? hi_h(m0) : lo_h(m0);
+                            const float c1 = half ? hi_h(m1) : lo_h(m1);
+                            const float X = fmaf(bb, c1, fmaf(a, c0, Ps[sidx]));
+                            const float Y = fmaf(e, c1, fmaf(d, c0, Rs[sidx]));
+                            const float2 tw = twiddle(j);
+                            red[lane * RS + j] = fmaf(tw.x, X, tw.y * Y);
+                        }
+                    }
+                }
+                float a4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+    #pragma unroll
+                for (int m = 0; m < 32; ++m)
+                    a4[m & 3] += red[(red_half + m) * RS + red_col];
+                float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+                if (NP == 64)
+                    acc = half_sum(acc);
+                s[h] = acc;
+            }
+        } else {
+            // Several query heads share the key tile: dequantize and rotate
+            // each (pair, token) once, U_j = T_j (x + i y) (times the field
+            // scale 2^(pos-24) and its inverse folded into T_j), then each
+            // head's term is Re[Q_h U_j] with Q_h = conj(q'_h) e^{i g G theta_i}.
+            float z0s[KC::NSCALE], z1s[KC::NSCALE];
 #pragma unroll
             for (int k = 0; k < KC::NSCALE; ++k) {
                 const float sc = 1.0f / (float)(1 << (24 - k * KB));
-                Ps[k] = P * sc;
-                Rs[k] = R * sc;
+                z0s[k] = z0 * sc;
+                z1s[k] = z1 * sc;
             }
+            float ux[G], uy[G];
 #pragma unroll
             for (int w = 0; w < S::WK; ++w) {
                 const uint32_t w0 = use.kw[w], w1 = use.kw[S::WK + w];
@@ -585,24 +613,33 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK, KB, VB)) void attend_kern
                     const int sidx = KC::pos(f) / KB;
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
-                        const int j = w * 2 * KC::TPH + half * KC::TPH + f;
+                        const int jj = w * 2 * KC::TPH + half * KC::TPH + f;
                         const float c0 = half ? hi_h(m0) : lo_h(m0);
                         const float c1 = half ? hi_h(m1) : lo_h(m1);
-                        const float X = fmaf(bb, c1, fmaf(a, c0, Ps[sidx]));
-                        const float Y = fmaf(e, c1, fmaf(d, c0, Rs[sidx]));
-                        const float2 tw = twiddle(j);
-                        red[lane * RS + j] = fmaf(tw.x, X, tw.y * Y);
+                        const float x = fmaf(s0, c0, z0s[sidx]);
+                        const float y = fmaf(s1, c1, z1s[sidx]);
+                        const float2 tw = twiddle(jj);  // (T.x, -T.y) * 2^(24-pos)
+                        ux[jj] = fmaf(tw.x, x, tw.y * y);
+                        uy[jj] = fmaf(tw.x, y, -(tw.y * x));
                     }
                 }
             }
-            float a4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
 #pragma unroll
-            for (int m = 0; m < 32; ++m)
-                a4[m & 3] += red[(red_half + m) * RS + red_col];
-            float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-            if (NP == 64)
-                acc = half_sum(acc);
-            s[h] = acc;
+            for (int h = 0; h < QPK; ++h) {
+                const float2 Q = cmul(qc[h], use.rg);
+                const float nqy = -Q.y;
+#pragma unroll
+                for (int jj = 0; jj < G; ++jj)
+                    red[lane * RS + jj] = fmaf(Q.x, ux[jj], nqy * uy[jj]);
+                float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < 32; ++m)
+                    a4[m & 3] += red[(red_half + m) * RS + red_col];
+                float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+                if (NP == 64)
+                    acc = half_sum(acc);
+                s[h] = acc;
+            }
         }
         softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, use.vw, use.vm, st);
         gb += stride;
@@ -739,7 +776,7 @@ void launch(const Planes& p, const void* q, float* out, int n, int splits, int n
             hipStream_t stream)
 {
     dim3 grid(splits, p.nb * p.hkv);
-    nwaves = nwaves < max_block_waves(QPK, KB, VB) ? nwaves : max_block_waves(QPK, KB, VB);
+    nwaves = nwaves < max_block_waves(QPK) ? nwaves : max_block_waves(QPK);
     attend_kernel<D, KB, VB, QPK><<<grid, 64 * nwaves, attend_lds_bytes<D, KB, VB, QPK>(nwaves),
                                     stream>>>(p, q, out, n, splits);
     if (splits > 1)

@@ -123,7 +123,7 @@ void attend_shape(const kvq* h, int n, int* splits_out, int* waves_out)
     const int full_groups = n / h->cfg.group;
     const int groups_per_step = 64 / (h->cfg.head_dim / 2);
     const int qpk = h->cfg.q_heads / h->cfg.kv_heads;
-    const int wpc = kvqi::max_block_waves(qpk, h->cfg.key_bits, h->cfg.value_bits);
+    const int wpc = kvqi::max_block_waves(qpk);
     const int cap = full_groups > 0 ? full_groups : 1;
     const int max_splits = h->layout.max_splits < cap ? h->layout.max_splits : cap;
     int splits = 0, waves = 0;

@@ -10,21 +10,9 @@ namespace kvqi {
 
 constexpr int kGroup = 32;  // G: tokens per key group, channels per value group
 
-// Attention kernel variants whose registers cannot hold the 32 per-token
-// twiddles of the rotary embedding read them from LDS instead: one query
-// head per KV head with 4- or 8-bit values or 8-bit keys.
-constexpr bool twiddles_in_lds(int qpk, int kbits, int vbits)
-{
-    return qpk == 1;
-}
-
-// Largest attention block in waves: 16 (up to 128 VGPRs per lane) with the
-// twiddles in LDS, 12 (up to 168) with them in registers and one query head
-// per KV head, 8 (up to 256) when several query heads share one.
-constexpr int max_block_waves(int qpk, int kbits, int vbits)
-{
-    return twiddles_in_lds(qpk, kbits, vbits) ? 16 : qpk == 1 ? 12 : 8;
-}
+// Largest attention block in waves: 16 (up to 128 VGPRs per lane) with one
+// query head per KV head, 8 (up to 256) when several query heads share one.
+constexpr int max_block_waves(int qpk) { return qpk == 1 ? 16 : 8; }
 
 // Everything a kernel needs to address the planes of one cache.
 struct Planes {
