@@ -121,6 +121,7 @@ constexpr int kDppXor1 = 0xb1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane k <-> 7-k within each 8
 constexpr int kDppMirror = 0x140;     // lane k <-> 15-k within each 16
+constexpr int kDppRor8 = 0x128;       // lane k <- lane (k+8) mod 16 within each 16
 
 // Cross-row exchanges on the VALU (no LDS round trip).  With both operands
 // equal to v, the 16-lane swap returns {rows (0,0,2,2) of v, rows (1,1,3,3)}
@@ -198,11 +199,18 @@ struct Shape {
     // the step and all 32 channels of value group r, so the weights it needs
     // sit in its own 16-lane row pair and one swap fetches both.  Otherwise
     // lane = (code word, token slot) as described at the top.
+    // Token quads (several query heads, head_dim 128): lane (r, c) takes
+    // tokens c, c^8, c+16 and (c^8)+16 of the step and code words
+    // (2r + c/8) * NW .. + NW-1 of each (16 channels of one value group);
+    // its weights come from one swap and two DPP row rotations.
     static constexpr bool PAIRS = (QPK == 1 && NP == 64);
-    static_assert(!PAIRS || NCG == 4, "one value group per 16-lane row");
-    static constexpr int NVW = PAIRS ? 2 * WV : VTOK;   // value code words per lane per step
-    static constexpr int NVM = PAIRS ? 2 : VTOK;        // value meta words per lane per step
-    static constexpr int NCL = PAIRS ? G : NC;          // value channels per lane
+    static constexpr bool QUADS = (QPK > 1 && NP == 64);
+    static_assert(!(PAIRS || QUADS) || NCG == 4, "value groups per 16-lane row");
+    static constexpr int NW = WPT / 8;                  // quads: words per (lane, token)
+    static constexpr int NVW = PAIRS ? 2 * WV : QUADS ? 4 * NW : VTOK;  // value code words per lane per step
+    static constexpr int NVM = PAIRS ? 2 : QUADS ? 4 : VTOK;            // value meta words per lane per step
+    static constexpr int NCL = PAIRS ? G : QUADS ? NW * NC : NC;        // value channels per lane
+    static constexpr int NRED = (QPK == 2 || QPK == 4) ? 2 : 1;  // reduce buffers per wave (heads alternate)
 };
 
 // Everything one wave step reads from memory, loaded one step ahead.
@@ -267,6 +275,29 @@ __device__ __forceinline__ void load_values(const HeadPlanes& hp, int lane, int 
                     vw[k * S::WV + u] = w[u];
             }
             vm[k] = vm0[tt * S::NCG + r];
+        }
+    } else if constexpr (S::QUADS) {
+        const unsigned r = lane >> 4, c = lane & 15;
+        const unsigned w0 = (2 * r + (c >> 3)) * S::NW, vg = w0 / S::WV;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // slots 0..3: tokens c, c^8, c+16, (c^8)+16
+            const unsigned tt = slot((k & 1 ? (c ^ 8u) : c) + (k & 2 ? 16u : 0u));
+            const uint32_t* src = vc0 + tt * S::WPT + w0;
+            if constexpr (S::NW == 1) {
+                vw[k] = src[0];
+            } else if constexpr (S::NW == 2) {
+                const uint2 w = *reinterpret_cast<const uint2*>(src);
+                vw[2 * k] = w.x;
+                vw[2 * k + 1] = w.y;
+            } else {
+                uint32_t w[S::NW];
+                load_words<S::NW>(src, w);
+#pragma unroll
+                for (int u = 0; u < S::NW; ++u)
+                    vw[k * S::NW + u] = w[u];
+            }
+            vm[k] = vm0[tt * S::NCG + vg];
         }
     } else {
         const unsigned w = lane % S::WPT, vslot = lane / S::WPT, vcg = w / S::WV;
@@ -350,6 +381,34 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
                     st.o[0][u * S::NC + f] = fmaf(ps, lo_h(m), st.o[0][u * S::NC + f]);
                     st.o[0][u * S::NC + C::TPH + f] =
                         fmaf(ps, hi_h(m), st.o[0][u * S::NC + C::TPH + f]);
+                }
+            }
+        }
+        return;
+    }
+    if constexpr (S::QUADS) {
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            // tokens c and c + 16 from the row pair, c^8 and (c^8) + 16 by
+            // rotating those by 8 lanes inside the row
+            const Pair pp = swap16(pw[h]);
+            const float pk[4] = {pp.a, dpp<kDppRor8>(pp.a), pp.b, dpp<kDppRor8>(pp.b)};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float pt = pk[k];  // 0 for absent tokens
+                const float ps = pt * lo_h(vmetas[k]);
+                st.z[h] = fmaf(pt, hi_h(vmetas[k]), st.z[h]);
+#pragma unroll
+                for (int u = 0; u < S::NW; ++u) {
+                    const uint32_t word = vwords[k * S::NW + u];
+                    const uint32_t wsh = word >> C::SHIFT;
+#pragma unroll
+                    for (int f = 0; f < C::TPH; ++f) {
+                        const uint32_t m = C::field(word, wsh, f);
+                        st.o[h][u * S::NC + f] = fmaf(ps, lo_h(m), st.o[h][u * S::NC + f]);
+                        st.o[h][u * S::NC + C::TPH + f] =
+                            fmaf(ps, hi_h(m), st.o[h][u * S::NC + C::TPH + f]);
+                    }
                 }
             }
         }
@@ -461,7 +520,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         for (int c = 0; c < S::NCL; ++c)
             st.o[h][c] = 0.f;
     }
-    float* red = smem + wave * 64 * RS;
+    float* red = smem + wave * S::NRED * 64 * RS;
     const int red_half = lane & ~31, red_col = lane & 31;
 
     if (do_tail && wave == nwaves - 1) {
@@ -626,15 +685,18 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
             }
 #pragma unroll
             for (int h = 0; h < QPK; ++h) {
+                // heads alternate between two buffers, so one head's writes
+                // need not wait for the previous head's reads
+                float* rb = red + (S::NRED > 1 ? (h & 1) : 0) * 64 * RS;
                 const float2 Q = cmul(qc[h], use.rg);
                 const float nqy = -Q.y;
 #pragma unroll
                 for (int jj = 0; jj < G; ++jj)
-                    red[lane * RS + jj] = fmaf(Q.x, ux[jj], nqy * uy[jj]);
+                    rb[lane * RS + jj] = fmaf(Q.x, ux[jj], nqy * uy[jj]);
                 float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int m = 0; m < 32; ++m)
-                    a4[m & 3] += red[(red_half + m) * RS + red_col];
+                    a4[m & 3] += rb[(red_half + m) * RS + red_col];
                 float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
                 if (NP == 64)
                     acc = half_sum(acc);
@@ -677,6 +739,28 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         if (lane == 0) {
             sm[wave] = st.m[0];
             sl[wave] = L;
+        }
+    } else if constexpr (S::QUADS) {
+        // lane (r, c) holds words (2r + c/8) * NW.. over its tokens: sum the
+        // 8 lanes that share them (c & 7 = 0..7)
+        const int w0 = (2 * (lane >> 4) + ((lane & 15) >> 3)) * S::NW;
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            const float L = wave_sum(st.l[h]);
+#pragma unroll
+            for (int c = 0; c < S::NCL; ++c) {
+                const float sc = (float)(1 << (24 - VC::pos(c % VC::TPH)));
+                float x = fmaf(st.o[h][c], sc, st.z[h]);
+                x += dpp<kDppXor1>(x);
+                x += dpp<kDppXor2>(x);
+                x += dpp<kDppHalfMirror>(x);
+                if ((lane & 7) == 0)
+                    so[(wave * QPK + h) * D + w0 * S::NC + c] = x;
+            }
+            if (lane == 0) {
+                sm[wave * QPK + h] = st.m[h];
+                sl[wave * QPK + h] = L;
+            }
         }
     } else {
         const int vw = lane % S::WPT, vslot = lane / S::WPT;
@@ -766,7 +850,7 @@ template <int D, int KB, int VB, int QPK>
 constexpr size_t attend_lds_bytes(int nwaves)
 {
     using S = Shape<D, KB, VB, QPK>;
-    const size_t red = (size_t)nwaves * 64 * S::RED_STRIDE;
+    const size_t red = (size_t)nwaves * S::NRED * 64 * S::RED_STRIDE;
     const size_t merge = 2 * kMaxWaves * QPK + (size_t)nwaves * QPK * D;
     return 4 * (red > merge ? red : merge);
 }
