@@ -70,7 +70,8 @@ KVQ_HD uint32_t double_to_half_bits(double x)
 
 struct GroupParams {
     double z, s, rinv;
-    uint32_t meta;  // step bits | zero bits << 16
+    float zf, rinvf;  // z exactly, 1/s rounded once to fp32
+    uint32_t meta;    // step bits | zero bits << 16
 };
 
 // Zero point and step of a group with minimum mn and maximum mx, each
@@ -86,6 +87,8 @@ KVQ_HD GroupParams group_params(float mn, float mx, int bits)
     g.z = half_bits_to_double(z16);
     g.s = half_bits_to_double(s16);
     g.rinv = (g.s != 0.0) ? 1.0 / g.s : 0.0;
+    g.zf = (float)g.z;
+    g.rinvf = (float)g.rinv;
     g.meta = s16 | (z16 << 16);
     return g;
 }
@@ -107,6 +110,85 @@ KVQ_HD uint32_t code_of(double x, const GroupParams& g, int top)
         c += (e > 0.0 ? 1.0 : -1.0);
     c = fmin(fmax(c, 0.0), (double)top);
     return (uint32_t)c;
+}
+
+// The same code through fp32 where fp32 decides it.  For x and z in binary16
+// or fp32, q32 = fl(fl(x - z) * fl(1/s)) carries three roundings, so
+// |q32 - q| <= 3.0001 * 2^-24 * |q|; when q32 is farther than
+// 2^-21 * (|q32| + 1) from every half-integer, q and q32 have the same
+// nearest integer and rint(q32) is the code.  q32 - rint(q32) is exact
+// (Sterbenz).  The rare elements inside that band take code_of.
+// The exact path for one element, from the group's fp64 parameters.  Kept
+// inline: the kernels branch to it rarely, and an out-of-line call gives
+// every wave a call frame to set up.
+KVQ_HD uint32_t code_of_exact(float x, double z, double s, double rinv, int top)
+{
+    GroupParams g;
+    g.z = z;
+    g.s = s;
+    g.rinv = rinv;
+    return code_of((double)x, g, top);
+}
+
+KVQ_HD uint32_t code_of_fast(float x, const GroupParams& g, int top)
+{
+    const float q = (x - g.zf) * g.rinvf;
+    const float c = rintf(q);
+    const float t = fabsf(q - c);
+    if (fabsf(t - 0.5f) <= 0x1p-21f * (fabsf(q) + 1.0f))
+        return code_of_exact(x, g.z, g.s, g.rinv, top);
+    return (uint32_t)fminf(fmaxf(c, 0.0f), (float)top);
+}
+
+// Quantize one group of 32 values and pack the codes LSB-first into B words,
+// the codes computed in fp32 as in code_of_fast.  A half-integer h changes a
+// clamped code only for h in [-0.5, 2^B - 1.5], where the fp32 quotient is
+// within 3 * 2^-24 * (2^B + 1) < 2^-21 * (2^B + 1) of the exact one.  For
+// B <= 4 the group keeps the largest |q - rint(q)| and is recomputed exactly
+// when that reaches 0.5 - 2^-21 * (2^B + 1); for B = 8 a large share of
+// groups would, so each element checks its own band (code_of_fast).
+template <int BITS>
+KVQ_HD uint32_t quantize_group(const float (&x)[32], uint32_t (&w)[BITS])
+{
+    constexpr int TOP = (1 << BITS) - 1;
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) {
+        mn = fminf(mn, x[j]);
+        mx = fmaxf(mx, x[j]);
+    }
+    const GroupParams gp = group_params(mn, mx, BITS);
+#pragma unroll
+    for (int i = 0; i < BITS; ++i)
+        w[i] = 0u;
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const uint32_t c = code_of_fast(x[j], gp, TOP);
+            w[(j * BITS) / 32] |= c << ((j * BITS) % 32);
+        }
+    } else {
+        float tmax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const float q = (x[j] - gp.zf) * gp.rinvf;
+            const float c = rintf(q);
+            tmax = fmaxf(tmax, fabsf(q - c));
+            const uint32_t ci = (uint32_t)fminf(fmaxf(c, 0.0f), (float)TOP);
+            w[(j * BITS) / 32] |= ci << ((j * BITS) % 32);
+        }
+        if (tmax >= 0.5f - 0x1p-21f * (float)(TOP + 2)) {
+#pragma unroll
+            for (int i = 0; i < BITS; ++i)
+                w[i] = 0u;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const uint32_t c = code_of_exact(x[j], gp.z, gp.s, gp.rinv, TOP);
+                w[(j * BITS) / 32] |= c << ((j * BITS) % 32);
+            }
+        }
+    }
+    return gp.meta;
 }
 
 }  // namespace kvqi

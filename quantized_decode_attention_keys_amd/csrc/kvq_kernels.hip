@@ -31,28 +31,6 @@ template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<__half>(__half x) { return __half2float(x); }
 
-// Quantize one group of G values held by one thread and pack it LSB-first.
-template <int BITS>
-__device__ __forceinline__ uint32_t quantize_pack(const float (&x)[G], uint32_t (&w)[G * BITS / 32])
-{
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int j = 1; j < G; ++j) {
-        mn = fminf(mn, x[j]);
-        mx = fmaxf(mx, x[j]);
-    }
-    const GroupParams gp = group_params(mn, mx, BITS);
-#pragma unroll
-    for (int i = 0; i < G * BITS / 32; ++i)
-        w[i] = 0u;
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const uint32_t c = code_of((double)x[j], gp, (1 << BITS) - 1);
-        w[(j * BITS) / 32] |= c << ((j * BITS) % 32);
-    }
-    return gp.meta;
-}
-
 // ------------------------------------------------------- prefill kernels --
 
 // One thread per (sequence*head, key group, channel): walks the group's G
@@ -76,7 +54,7 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(Planes p, const T* __re
     for (int j = 0; j < G; ++j)
         x[j] = to_f32(src[(size_t)j * D]);
     uint32_t w[WK];
-    const uint32_t meta = quantize_pack<BITS>(x, w);
+    const uint32_t meta = quantize_group<BITS>(x, w);
     const size_t gc = (bh * p.gcap + g) * D + c;
     uint32_t* dst = p.k_codes + gc * WK;
 #pragma unroll
@@ -125,7 +103,7 @@ __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __
     for (int j = 0; j < G; ++j)
         x[j] = to_f32(src[j]);
     uint32_t w[WV];
-    const uint32_t meta = quantize_pack<BITS>(x, w);
+    const uint32_t meta = quantize_group<BITS>(x, w);
     const size_t tc = (bh * p.tcap + t_dst0 + t) * ncg + cg;
     uint32_t* dst = p.v_codes + tc * WV;
 #pragma unroll
@@ -163,7 +141,7 @@ __global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __rest
         }
         const GroupParams gp = group_params(mn, mx, VBITS);
         const int j = c % G;
-        uint32_t bits = code_of((double)x, gp, (1 << VBITS) - 1) << ((j * VBITS) % 32);
+        uint32_t bits = code_of_fast(x, gp, (1 << VBITS) - 1) << ((j * VBITS) % 32);
 #pragma unroll
         for (int off = CPW / 2; off >= 1; off >>= 1)
             bits |= __shfl_xor(bits, off);
@@ -186,7 +164,7 @@ __global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __rest
         x[j] = to_f32(tail[(bh * G + j) * D + c]);
     x[G - 1] = to_f32(val);
     uint32_t w[WK];
-    const uint32_t meta = quantize_pack<KBITS>(x, w);
+    const uint32_t meta = quantize_group<KBITS>(x, w);
     const size_t gc = (bh * p.gcap + n / G) * D + c;
     uint32_t* dst = p.k_codes + gc * WK;
 #pragma unroll

@@ -5,9 +5,28 @@
 extern "C" {
 uint32_t shim_double_to_half(double x) { return kvqi::double_to_half_bits(x); }
 double shim_half_to_double(uint32_t h) { return kvqi::half_bits_to_double(h); }
-// Quantize one group of n floats exactly as the kernels do; returns the meta
-// word and writes the codes.
+// Quantize one group of n = 32 floats with the kernels' group quantizer;
+// returns the meta word and writes the unpacked codes.
 uint32_t shim_quant_group(const float* x, int n, int bits, uint8_t* codes)
+{
+    if (n != 32)
+        return 0xffffffffu;
+    float xs[32];
+    for (int i = 0; i < 32; ++i)
+        xs[i] = x[i];
+    uint32_t w[8] = {0}, meta = 0;
+    switch (bits) {
+    case 2: meta = kvqi::quantize_group<2>(xs, *reinterpret_cast<uint32_t(*)[2]>(w)); break;
+    case 4: meta = kvqi::quantize_group<4>(xs, *reinterpret_cast<uint32_t(*)[4]>(w)); break;
+    case 8: meta = kvqi::quantize_group<8>(xs, *reinterpret_cast<uint32_t(*)[8]>(w)); break;
+    }
+    for (int i = 0; i < n; ++i)
+        codes[i] = (uint8_t)((w[(i * bits) / 32] >> ((i * bits) % 32)) & ((1u << bits) - 1u));
+    return meta;
+}
+// The exact fp64 code alone, and the number of elements of a group that the
+// fp32 path hands to it.
+uint32_t shim_quant_group_exact(const float* x, int n, int bits, uint8_t* codes)
 {
     float mn = x[0], mx = x[0];
     for (int i = 1; i < n; ++i) {
@@ -18,5 +37,21 @@ uint32_t shim_quant_group(const float* x, int n, int bits, uint8_t* codes)
     for (int i = 0; i < n; ++i)
         codes[i] = (uint8_t)kvqi::code_of((double)x[i], g, (1 << bits) - 1);
     return g.meta;
+}
+int shim_fallbacks(const float* x, int n, int bits)
+{
+    float mn = x[0], mx = x[0];
+    for (int i = 1; i < n; ++i) {
+        mn = fminf(mn, x[i]);
+        mx = fmaxf(mx, x[i]);
+    }
+    const kvqi::GroupParams g = kvqi::group_params(mn, mx, bits);
+    int k = 0;
+    for (int i = 0; i < n; ++i) {
+        const float q = (x[i] - g.zf) * g.rinvf;
+        const float t = fabsf(q - rintf(q));
+        k += fabsf(t - 0.5f) <= 0x1p-21f * (fabsf(q) + 1.0f);
+    }
+    return k;
 }
 }

@@ -24,8 +24,11 @@ def shim(tmp_path_factory):
     L.shim_double_to_half.restype = ctypes.c_uint32
     L.shim_half_to_double.argtypes = [ctypes.c_uint32]
     L.shim_half_to_double.restype = ctypes.c_double
-    L.shim_quant_group.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    L.shim_quant_group.restype = ctypes.c_uint32
+    for f in (L.shim_quant_group, L.shim_quant_group_exact):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        f.restype = ctypes.c_uint32
+    L.shim_fallbacks.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    L.shim_fallbacks.restype = ctypes.c_int
     return L
 
 
@@ -66,10 +69,47 @@ def test_group_codes_match_oracle(shim, orc, bits, dt):
         x = np.concatenate([[z, z + top * s], z + (rng.integers(0, top, 30) + 0.5) * s])
         groups.append(x.astype(dt))
     groups.append(np.full(32, 1.25, dtype=dt))
+    groups += _near_ties(rng, bits, dt)
+    fallbacks = 0
     for x in groups:
         xf = np.ascontiguousarray(x.astype(np.float32))
-        codes = np.zeros(32, dtype=np.uint8)
-        meta = shim.shim_quant_group(xf.ctypes.data, 32, bits, codes.ctypes.data)
         oc, s16, z16 = orc.quant_group(x.astype(np.float64), bits)
-        assert meta == (s16 | (z16 << 16))
-        assert np.array_equal(codes, oc)
+        for fn in (shim.shim_quant_group, shim.shim_quant_group_exact):
+            codes = np.zeros(32, dtype=np.uint8)
+            meta = fn(xf.ctypes.data, 32, bits, codes.ctypes.data)
+            assert meta == (s16 | (z16 << 16))
+            assert np.array_equal(codes, oc)
+        fallbacks += shim.shim_fallbacks(xf.ctypes.data, 32, bits)
+    # the near-tie groups reach the exact path; random data almost never does
+    assert fallbacks > 0
+
+
+def _near_ties(rng, bits, dt):
+    """Groups whose elements sit at, or a few units in the last place of the
+    input type away from, half-integer multiples of the step: the band where
+    the fp32 path hands the element to the exact path, and just outside it."""
+    out = []
+    top = 2 ** bits - 1
+    for _ in range(400):
+        mn = float(dt(rng.uniform(-50, 50)))
+        mx = float(dt(mn + abs(rng.standard_normal()) * 10.0 ** rng.uniform(-3, 2) + 1e-3))
+        s = float(np.float16((mx - mn) / top))
+        z = float(np.float16(mn))
+        if not (s > 0 and np.isfinite(s)):
+            continue
+        k = rng.integers(0, top, 30)
+        x = (z + (k + 0.5) * s).astype(dt)
+        steps = rng.integers(-3, 4, 30)
+        x = np.array([_nudge(v, st, dt) for v, st in zip(x, steps)], dtype=dt)
+        x = np.concatenate([np.array([mn, mx], dtype=dt), x])
+        x = np.clip(x, dt(mn), dt(mx))
+        out.append(x)
+    return out
+
+
+def _nudge(v, steps, dt):
+    v = dt(v)
+    d = dt(np.inf) if steps > 0 else dt(-np.inf)
+    for _ in range(abs(int(steps))):
+        v = np.nextafter(v, d, dtype=dt)
+    return v

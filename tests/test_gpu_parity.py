@@ -49,6 +49,33 @@ def test_d128_gqa_ragged(qpk, dtype):
     _attend_both(cfg, cache, op, gp, n)
 
 
+@pytest.mark.parametrize("bits", [(4, 4), (8, 8), (4, 2), (2, 4), (2, 8), (8, 2)])
+@pytest.mark.parametrize("qpk", [1, 2, 4])
+def test_d128_bits_ragged(bits, qpk):
+    """head_dim 128 at every key/value width pair the value-lane mappings
+    depend on (words per token row, words per lane), n = 1000."""
+    cfg = synth.scaled(synth.CONFIGS["llama2_7b"], batch=2, kv_heads=2, q_heads=2 * qpk,
+                       n_tokens=1000, key_bits=bits[0], value_bits=bits[1])
+    n = 1000
+    cache, k, v = run_prefill(cfg, n, max_tokens=1024)
+    gp = gpu_planes(cache)
+    op = oracle_planes(cfg, k, v, 1024)
+    assert_planes_equal(gp, op, n)
+    _attend_both(cfg, cache, op, gp, n)
+
+
+@pytest.mark.parametrize("bits", [(2, 2), (4, 4), (8, 8)])
+@pytest.mark.parametrize("qpk", [2, 4])
+def test_d64_gqa(bits, qpk):
+    cfg = synth.scaled(TINY, kv_heads=2, q_heads=2 * qpk, key_bits=bits[0], value_bits=bits[1])
+    n = 300
+    cache, k, v = run_prefill(cfg, n, max_tokens=320)
+    gp = gpu_planes(cache)
+    op = oracle_planes(cfg, k, v, 320)
+    assert_planes_equal(gp, op, n)
+    _attend_both(cfg, cache, op, gp, n)
+
+
 def test_append_through_tail_and_flushes():
     """Prefill 250 tokens, append 40 one at a time (flushes at n = 256 and
     288); planes equal the oracle's one-shot quantization of all tokens and
