@@ -607,28 +607,28 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         const float s1 = h2f(use.km.y), z1 = h2f(use.km.y >> 16);
         float s[QPK];
         if constexpr (QPK == 1) {
-    #pragma unroll
+#pragma unroll
             for (int h = 0; h < QPK; ++h) {
                 const float2 Q = cmul(qc[h], use.rg);
                 // X = P + a c0 + bb c1 = Re[Q (x+iy)],  Y = R + d c0 + e c1 = Im[Q (x+iy)]
                 const float P = Q.x * z0 - Q.y * z1, a = Q.x * s0, bb = -Q.y * s1;
                 const float R = Q.y * z0 + Q.x * z1, d = Q.y * s0, e = Q.x * s1;
                 float Ps[KC::NSCALE], Rs[KC::NSCALE];
-    #pragma unroll
+#pragma unroll
                 for (int k = 0; k < KC::NSCALE; ++k) {
                     const float sc = 1.0f / (float)(1 << (24 - k * KB));
                     Ps[k] = P * sc;
                     Rs[k] = R * sc;
                 }
-    #pragma unroll
+#pragma unroll
                 for (int w = 0; w < S::WK; ++w) {
                     const uint32_t w0 = use.kw[w], w1 = use.kw[S::WK + w];
                     const uint32_t w0s = w0 >> KC::SHIFT, w1s = w1 >> KC::SHIFT;
-    #pragma unroll
+#pragma unroll
                     for (int f = 0; f < KC::TPH; ++f) {
                         const uint32_t m0 = KC::field(w0, w0s, f), m1 = KC::field(w1, w1s, f);
                         const int sidx = KC::pos(f) / KB;
-    #pragma unroll
+#pragma unroll
                         for (int half = 0; half < 2; ++half) {
                             const int j = w * 2 * KC::TPH + half * KC::TPH + f;
                             const float c0 = half ? hi_h(m0) : lo_h(m0);
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                     }
                 }
                 float a4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
-    #pragma unroll
+#pragma unroll
                 for (int m = 0; m < 32; ++m)
                     a4[m & 3] += red[(red_half + m) * RS + red_col];
                 float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
