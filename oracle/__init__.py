@@ -59,14 +59,16 @@ def lib() -> ctypes.CDLL:
         L.orc_unpack.restype = None
         L.orc_code_at.argtypes = [P, i, i]
         L.orc_code_at.restype = i
-        L.orc_quantize_keys.argtypes = [P, i, i, i, i, i, i, i, i, P, P, P]
+        L.orc_quantized_tokens.argtypes = [i, i, i]
+        L.orc_quantized_tokens.restype = i
+        L.orc_quantize_keys.argtypes = [P, i, i, i, i, i, i, i, i, i, P, P, P]
         L.orc_quantize_keys.restype = i
-        L.orc_quantize_values.argtypes = [P, i, i, i, i, i, i, i, i, P, P]
+        L.orc_quantize_values.argtypes = [P, i, i, i, i, i, i, i, i, i, P, P, P]
         L.orc_quantize_values.restype = i
         L.orc_rope.argtypes = [P, i, d, d]
         L.orc_rope.restype = None
-        L.orc_attend.argtypes = [i, i, i, i, i, i, i, i, i, d, P, P, P, P, P,
-                                 i, P, i, i, i, P]
+        L.orc_attend.argtypes = [i, i, i, i, i, i, i, i, i, i, d, P, P, P, P, P,
+                                 P, i, P, i, i, i, P]
         L.orc_attend.restype = i
         L.orc_attend_dense.argtypes = [i, i, i, i, d, P, P, i, P, i, i, i, P]
         L.orc_attend_dense.restype = i
@@ -125,48 +127,61 @@ def unpack(words, n: int, bits: int) -> np.ndarray:
     return codes
 
 
-def plane_shapes(nb, hkv, D, G, kbits, vbits, max_tokens):
-    """Shapes of the packed planes for a cache of capacity max_tokens."""
+def quantized_tokens(n: int, G: int = 32, residual: int = 0) -> int:
+    """Tq: tokens [0, Tq) are quantized, [Tq, n) held in full precision."""
+    return lib().orc_quantized_tokens(n, G, residual)
+
+
+def plane_shapes(nb, hkv, D, G, kbits, vbits, max_tokens, residual=0):
+    """Shapes of the packed planes for a cache of capacity max_tokens.  The
+    key tail (and with residual > 0 the value tail) is a ring of
+    residual + G token slots."""
     gcap = -(-max_tokens // G)
     tcap = gcap * G
+    ring = residual + G
     return {
         "k_codes": (nb, hkv, gcap, D, G * kbits // 32),
         "k_meta": (nb, hkv, gcap, D),
         "v_codes": (nb, hkv, tcap, D // G, G * vbits // 32),
         "v_meta": (nb, hkv, tcap, D // G),
-        "k_tail": (nb, hkv, G, D),
+        "k_tail": (nb, hkv, ring, D),
+        "v_tail": (nb, hkv, ring if residual > 0 else 0, D),
     }
 
 
-def quantize_keys(k: np.ndarray, bits: int, G: int = 32, max_tokens=None):
+def quantize_keys(k: np.ndarray, bits: int, G: int = 32, max_tokens=None, residual=0):
     """Key planes for k[nb][Hkv][T][D]: (k_codes, k_meta, k_tail)."""
     k = np.ascontiguousarray(k)
     nb, hkv, T, D = k.shape
     cap = T if max_tokens is None else max_tokens
-    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1))
+    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1), residual)
     kc = np.zeros(sh["k_codes"], dtype=np.uint32)
     km = np.zeros(sh["k_meta"], dtype=np.uint32)
     kt = np.zeros(sh["k_tail"], dtype=k.dtype)
     rc = lib().orc_quantize_keys(_ptr(k), _dtype_code(k), nb, hkv, T, D, G,
-                                 bits, sh["k_meta"][2], _ptr(kc), _ptr(km), _ptr(kt))
+                                 bits, residual, sh["k_meta"][2], _ptr(kc), _ptr(km),
+                                 _ptr(kt))
     if rc != 0:
         raise ValueError("orc_quantize_keys failed")
     return kc, km, kt
 
 
-def quantize_values(v: np.ndarray, bits: int, G: int = 32, max_tokens=None):
-    """Value planes for v[nb][Hkv][T][D]: (v_codes, v_meta)."""
+def quantize_values(v: np.ndarray, bits: int, G: int = 32, max_tokens=None, residual=0):
+    """Value planes for v[nb][Hkv][T][D]: (v_codes, v_meta), and the value
+    tail ring third when residual > 0."""
     v = np.ascontiguousarray(v)
     nb, hkv, T, D = v.shape
     cap = T if max_tokens is None else max_tokens
-    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1))
+    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1), residual)
     vc = np.zeros(sh["v_codes"], dtype=np.uint32)
     vm = np.zeros(sh["v_meta"], dtype=np.uint32)
+    vt = np.zeros(sh["v_tail"], dtype=v.dtype)
     rc = lib().orc_quantize_values(_ptr(v), _dtype_code(v), nb, hkv, T, D, G,
-                                   bits, sh["v_meta"][2], _ptr(vc), _ptr(vm))
+                                   bits, residual, sh["v_meta"][2], _ptr(vc), _ptr(vm),
+                                   _ptr(vt) if residual > 0 else None)
     if rc != 0:
         raise ValueError("orc_quantize_values failed")
-    return vc, vm
+    return (vc, vm, vt) if residual > 0 else (vc, vm)
 
 
 # ---------------------------------------------------------------- attention
@@ -178,12 +193,14 @@ def rope(u, p: float, base: float = 10000.0) -> np.ndarray:
 
 
 def attend(planes: dict, q: np.ndarray, n: int, kbits: int, vbits: int,
-           hkv: int, G: int = 32, base: float = 10000.0, rows=None) -> np.ndarray:
+           hkv: int, G: int = 32, base: float = 10000.0, rows=None,
+           residual: int = 0) -> np.ndarray:
     """Decode attention over quantized planes for queries q[nb][Hq][D].
 
-    ``planes`` holds k_codes, k_meta, k_tail, v_codes, v_meta (numpy).  The
-    tail's element type is q's.  ``rows`` = (begin, end) over b*Hq + hq.
-    Returns float64 [rows, D] (all rows: reshaped to [nb, Hq, D])."""
+    ``planes`` holds k_codes, k_meta, k_tail, v_codes, v_meta (numpy), and
+    v_tail when residual > 0.  The tails' element type is q's.  ``rows`` =
+    (begin, end) over b*Hq + hq.  Returns float64 [rows, D] (all rows:
+    reshaped to [nb, Hq, D])."""
     q = np.ascontiguousarray(q)
     nb, hq, D = q.shape
     kc = np.ascontiguousarray(planes["k_codes"], dtype=np.uint32)
@@ -192,13 +209,18 @@ def attend(planes: dict, q: np.ndarray, n: int, kbits: int, vbits: int,
     kt = np.ascontiguousarray(kt)
     vc = np.ascontiguousarray(planes["v_codes"], dtype=np.uint32)
     vm = np.ascontiguousarray(planes["v_meta"], dtype=np.uint32)
+    vt = None
+    if residual > 0:
+        vt = np.ascontiguousarray(np.ascontiguousarray(planes["v_tail"]).astype(q.dtype,
+                                                                              copy=False))
     gcap = km.shape[2]
     tcap = vm.shape[2]
     r0, r1 = (0, nb * hq) if rows is None else rows
     out = np.zeros((r1 - r0, D), dtype=np.float64)
-    rc = lib().orc_attend(nb, hq, hkv, D, G, kbits, vbits, gcap, tcap, float(base),
-                          _ptr(kc), _ptr(km), _ptr(kt), _ptr(vc), _ptr(vm),
-                          _dtype_code(q), _ptr(q), n, r0, r1, _ptr(out))
+    rc = lib().orc_attend(nb, hq, hkv, D, G, kbits, vbits, residual, gcap, tcap,
+                          float(base), _ptr(kc), _ptr(km), _ptr(kt), _ptr(vc), _ptr(vm),
+                          _ptr(vt) if vt is not None else None, _dtype_code(q), _ptr(q),
+                          n, r0, r1, _ptr(out))
     if rc != 0:
         raise ValueError("orc_attend failed")
     if rows is None:

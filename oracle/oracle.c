@@ -31,6 +31,12 @@
  *      Breaks"]; [GEOM, "Stop Obsessing Over Bits"].
  *   3. Key tokens that do not yet fill a G-token group stay unquantized in
  *      a tail buffer.  [BITS, "The Systems Tax, and Why It Is Not a Detail"].
+ *      Residual window R (KIVI keeps the most recent tokens in full
+ *      precision; [BITS], same section): with R > 0, keys and values of
+ *      tokens [Tq, n) stay unquantized, Tq = G * floor(max(0, n - R) / G), so
+ *      at least R (at most R + G - 1) recent tokens; a G-block is quantized
+ *      when it leaves the window.  R = 0: Tq = G * floor(n / G) for keys and
+ *      every value is quantized on arrival.
  *   4. Keys are stored before the rotary position embedding; the rotation is
  *      applied after dequantization.  [BITS, "Rotary Embeddings Complicate
  *      the Keys"]; [GEOM, "What Data Scientists Should Do Next"].
@@ -50,7 +56,9 @@
  *   V_CODES u32[nb][Hkv][Tcap][D/G][Wv] channel j of a channel group at bits
  *                                       [j*Bv, j*Bv+Bv)
  *   V_META  u32[nb][Hkv][Tcap][D/G]     binary16 step | binary16 zero << 16
- *   K_TAIL  dtype[nb][Hkv][G][D]        slot j = token Tq + j, verbatim
+ *   K_TAIL  dtype[nb][Hkv][R+G][D]      ring: token t >= Tq in slot t mod (R+G),
+ *                                       verbatim (R = 0: slot t - Tq)
+ *   V_TAIL  dtype[nb][Hkv][R+G][D]      the same for values (R > 0 only)
  *
  * Input element types: ORC_F16 (IEEE binary16 bit patterns) or ORC_F32.
  */
@@ -194,18 +202,29 @@ void orc_unpack(const uint32_t* words, int n, int bits, uint8_t* codes)
         codes[j] = (uint8_t)orc_code_at(words, j, bits);
 }
 
-/* Key planes for T cached tokens: groups g < T/G are quantized per channel
- * (group = one channel over tokens gG .. gG+G-1); tokens from Tq = (T/G)*G
- * on are copied verbatim into the tail.  Planes sized for gcap groups. */
+/* First token of the unquantized region of a cache of n tokens with
+ * residual window R (step 3 above). */
+int orc_quantized_tokens(int n, int G, int R)
+{
+    int a = n - R;
+    return a > 0 ? (a / G) * G : 0;
+}
+
+/* Key planes for T cached tokens with residual window R: groups g < Tq/G
+ * are quantized per channel (group = one channel over tokens gG .. gG+G-1);
+ * tokens t >= Tq are copied verbatim into ring slot t mod (R+G) of the tail.
+ * Planes sized for gcap groups. */
 int orc_quantize_keys(const void* k, int dtype, int nb, int hkv, int T, int D,
-                      int G, int bits, int gcap, uint32_t* k_codes,
+                      int G, int bits, int R, int gcap, uint32_t* k_codes,
                       uint32_t* k_meta, void* k_tail)
 {
-    if (G <= 0 || (G * bits) % 32 != 0 || T < 0 || T / G > gcap)
+    if (G <= 0 || (G * bits) % 32 != 0 || T < 0 || R < 0 || R % G != 0 ||
+        T / G > gcap)
         return -1;
     int wk = G * bits / 32;
-    int ngroups = T / G;
-    int tq = ngroups * G;
+    int tq = orc_quantized_tokens(T, G, R);
+    int ngroups = tq / G;
+    int ring = R + G;
     size_t esz = (dtype == ORC_F16) ? 2 : 4;
     double* x = (double*)malloc(sizeof(double) * (size_t)G);
     uint8_t* codes = (uint8_t*)malloc((size_t)G);
@@ -229,7 +248,7 @@ int orc_quantize_keys(const void* k, int dtype, int nb, int hkv, int T, int D,
                     k_meta[gc] = (uint32_t)s16 | ((uint32_t)z16 << 16);
                 }
             for (int t = tq; t < T; ++t)
-                memcpy((char*)k_tail + ((bh * G + (t - tq)) * D) * esz,
+                memcpy((char*)k_tail + ((bh * ring + t % ring) * D) * esz,
                        (const char*)k + ((bh * T + t) * D) * esz, esz * D);
         }
     free(x);
@@ -237,16 +256,22 @@ int orc_quantize_keys(const void* k, int dtype, int nb, int hkv, int T, int D,
     return 0;
 }
 
-/* Value planes for T tokens: every token is quantized at once, per channel
- * group (group = channels cg*G .. cg*G+G-1 of one token). */
+/* Value planes for T tokens, per channel group (group = channels
+ * cg*G .. cg*G+G-1 of one token).  R = 0: every token is quantized.  R > 0:
+ * tokens t < Tq are quantized and tokens t >= Tq copied verbatim into ring
+ * slot t mod (R+G) of v_tail. */
 int orc_quantize_values(const void* v, int dtype, int nb, int hkv, int T,
-                        int D, int G, int bits, int tcap, uint32_t* v_codes,
-                        uint32_t* v_meta)
+                        int D, int G, int bits, int R, int tcap,
+                        uint32_t* v_codes, uint32_t* v_meta, void* v_tail)
 {
-    if (G <= 0 || D % G != 0 || (G * bits) % 32 != 0 || T < 0 || T > tcap)
+    if (G <= 0 || D % G != 0 || (G * bits) % 32 != 0 || T < 0 || T > tcap ||
+        R < 0 || R % G != 0 || (R > 0 && !v_tail))
         return -1;
     int wv = G * bits / 32;
     int ncg = D / G;
+    int tq = R > 0 ? orc_quantized_tokens(T, G, R) : T;
+    int ring = R + G;
+    size_t esz = (dtype == ORC_F16) ? 2 : 4;
     double* x = (double*)malloc(sizeof(double) * (size_t)G);
     uint8_t* codes = (uint8_t*)malloc((size_t)G);
     if (!x || !codes) {
@@ -257,7 +282,7 @@ int orc_quantize_values(const void* v, int dtype, int nb, int hkv, int T,
     for (int b = 0; b < nb; ++b)
         for (int h = 0; h < hkv; ++h) {
             size_t bh = (size_t)b * hkv + h;
-            for (int t = 0; t < T; ++t)
+            for (int t = 0; t < tq; ++t)
                 for (int cg = 0; cg < ncg; ++cg) {
                     for (int j = 0; j < G; ++j)
                         x[j] = load_elem(v, dtype,
@@ -268,6 +293,9 @@ int orc_quantize_values(const void* v, int dtype, int nb, int hkv, int T,
                     orc_pack(codes, G, bits, v_codes + tc * wv);
                     v_meta[tc] = (uint32_t)s16 | ((uint32_t)z16 << 16);
                 }
+            for (int t = tq; t < T; ++t)
+                memcpy((char*)v_tail + ((bh * ring + t % ring) * D) * esz,
+                       (const char*)v + ((bh * T + t) * D) * esz, esz * D);
         }
     free(x);
     free(codes);
@@ -325,20 +353,25 @@ static void softmax_sum(const double* score, const double* vals, int n, int D,
  * for the output rows r in [row_begin, row_end), r = b*Hq + hq.  Query head
  * hq reads KV head hq / (Hq/Hkv).  out holds (row_end-row_begin) x D doubles.
  *   keys t < Tq: dequantize per channel group, then rotate to position t;
- *   keys t >= Tq: tail slot t - Tq, rotated to position t;
+ *   keys t >= Tq: tail ring slot t mod (R+G), rotated to position t;
+ *   values t < Tq (all t when R = 0): dequantize; else v_tail ring slot;
  *   query: rotated to position n-1;
  *   score_t = q'.k'_t / sqrt(D); out = sum_t softmax(score)_t * vhat_t. */
 int orc_attend(int nb, int hq, int hkv, int D, int G, int kbits, int vbits,
-               int gcap, int tcap, double base, const uint32_t* k_codes,
+               int R, int gcap, int tcap, double base, const uint32_t* k_codes,
                const uint32_t* k_meta, const void* k_tail,
-               const uint32_t* v_codes, const uint32_t* v_meta, int dtype,
-               const void* q, int n, int row_begin, int row_end, double* out)
+               const uint32_t* v_codes, const uint32_t* v_meta,
+               const void* v_tail, int dtype, const void* q, int n,
+               int row_begin, int row_end, double* out)
 {
     if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 || D % G != 0 ||
-        n > tcap || n / G > gcap || row_begin < 0 || row_end > nb * hq)
+        n > tcap || n / G > gcap || row_begin < 0 || row_end > nb * hq ||
+        R < 0 || R % G != 0 || (R > 0 && !v_tail))
         return -1;
     int wk = G * kbits / 32, wv = G * vbits / 32, ncg = D / G;
-    int tq = (n / G) * G;
+    int tq = orc_quantized_tokens(n, G, R);
+    int vq = R > 0 ? tq : n;
+    int ring = R + G;
     double* score = (double*)malloc(sizeof(double) * (size_t)n);
     double* vals = (double*)malloc(sizeof(double) * (size_t)n * D);
     double* qr = (double*)malloc(sizeof(double) * (size_t)D);
@@ -366,19 +399,25 @@ int orc_attend(int nb, int hq, int hkv, int D, int G, int kbits, int vbits,
             } else {
                 for (int c = 0; c < D; ++c)
                     kr[c] = load_elem(k_tail, dtype,
-                                      (bh * G + (t - tq)) * D + c);
+                                      (bh * ring + t % ring) * D + c);
             }
             orc_rope(kr, D, (double)t, base);
             double dot = 0.0;
             for (int c = 0; c < D; ++c)
                 dot += qr[c] * kr[c];
             score[t] = dot / sqrt((double)D);
-            for (int cg = 0; cg < ncg; ++cg) {
-                size_t tc = (bh * tcap + t) * ncg + cg;
-                orc_unpack(v_codes + tc * wv, G, vbits, codes);
-                for (int j = 0; j < G; ++j)
-                    vals[(size_t)t * D + cg * G + j] =
-                        dequant(v_meta[tc], codes[j]);
+            if (t < vq) {
+                for (int cg = 0; cg < ncg; ++cg) {
+                    size_t tc = (bh * tcap + t) * ncg + cg;
+                    orc_unpack(v_codes + tc * wv, G, vbits, codes);
+                    for (int j = 0; j < G; ++j)
+                        vals[(size_t)t * D + cg * G + j] =
+                            dequant(v_meta[tc], codes[j]);
+                }
+            } else {
+                for (int c = 0; c < D; ++c)
+                    vals[(size_t)t * D + c] =
+                        load_elem(v_tail, dtype, (bh * ring + t % ring) * D + c);
             }
         }
         softmax_sum(score, vals, n, D, out + (size_t)(r - row_begin) * D);
