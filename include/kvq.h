@@ -54,8 +54,18 @@
  *   V_CODES u32[batch][kv_heads][Tcap][head_dim/G][Wv]
  *           code of channel cg*G + j of token t at bits [j*value_bits, ...)
  *   V_META  u32[batch][kv_heads][Tcap][head_dim/G]   (as K_META)
- *   K_TAIL  dtype[batch][kv_heads][G][head_dim]
- *           slot j holds key token Tq + j verbatim, Tq = floor(n/G)*G
+ *   K_TAIL  dtype[batch][kv_heads][R+G][head_dim]
+ *           ring: key token t >= Tq verbatim in slot t mod (R+G)
+ *   V_TAIL  dtype[batch][kv_heads][R+G][head_dim]   (R > 0 only, else empty)
+ *           ring: value token t >= Tq verbatim in slot t mod (R+G)
+ * Residual window R = kvq_config.residual (the page "Your KV Cache Doesn't
+ * Have a Bit Problem...", section "The Systems Tax, and Why It Is Not a
+ * Detail": KIVI keeps the most recent tokens in full precision).  Tokens
+ * [0, Tq) are quantized, Tq = G * floor(max(0, n - R) / G); tokens [Tq, n)
+ * stay in full precision: their keys always, their values when R > 0 (with
+ * R = 0 every value is quantized on arrival and only the < G keys of the
+ * unfilled group wait).  With R > 0 at least R and at most R + G - 1 recent
+ * tokens are unquantized; a G-block is quantized when it leaves the window.
  * The step and zero are each rounded once, to nearest-even, from the exact
  * value (range/(2^B-1) and the minimum); the code of x is the integer nearest
  * to (x - zero)/step computed exactly, ties to even, clamped to
@@ -101,14 +111,17 @@ typedef struct kvq_config {
     int32_t value_bits; /* 2, 4 or 8                                        */
     int32_t dtype;      /* KVQ_F16 or KVQ_F32                               */
     float rope_base;    /* > 1, e.g. 10000                                  */
+    int32_t residual;   /* R: recent tokens kept in full precision, a
+                           multiple of group in [0, 1024]; 0 = none         */
 } kvq_config;
 
 typedef struct kvq_layout {
-    size_t k_codes, k_meta, v_codes, v_meta, k_tail; /* byte offsets        */
+    size_t k_codes, k_meta, v_codes, v_meta, k_tail, v_tail; /* byte offsets */
     size_t rope_group, rope_offset, partials;
     size_t total_bytes;   /* == kvq_workspace_bytes(cfg)                     */
     int32_t gcap, tcap;   /* Gcap and Tcap above                             */
     int32_t max_splits;   /* token splits per (sequence, KV head) at most    */
+    int32_t tail_slots;   /* R + G: slots of each tail ring                  */
 } kvq_layout;
 
 typedef struct kvq kvq_t; /* opaque; lives in host memory */
@@ -129,9 +142,11 @@ int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes,
 
 /* Quantize a whole prompt of n_tokens tokens into the empty cache.
  * d_k, d_v: dtype[batch][kv_heads][n_tokens][head_dim], keys before the
- * rotary embedding.  Key groups g < n_tokens/G are quantized per channel
- * (K_CODES, K_META); the last n_tokens mod G keys go to K_TAIL; every value
- * token is quantized per channel group (V_CODES, V_META).  Sets n = n_tokens.
+ * rotary embedding.  With Tq as above for n = n_tokens: key groups
+ * g < Tq/G are quantized per channel (K_CODES, K_META) and keys t >= Tq go to
+ * the K_TAIL ring; R = 0: every value token is quantized per channel group
+ * (V_CODES, V_META); R > 0: values t < Tq are quantized and values t >= Tq
+ * go to the V_TAIL ring.  Sets n = n_tokens.
  * n_tokens == 0 is allowed and enqueues nothing.
  * Errors: KVQ_ERR_ARG (null handle or pointers with n_tokens > 0, negative
  * n_tokens), KVQ_ERR_STATE (n != 0), KVQ_ERR_CAPACITY (n_tokens >
@@ -140,9 +155,13 @@ int kvq_quantize_prefill(kvq_t* h, const void* d_k, const void* d_v,
                          int32_t n_tokens, void* stream);
 
 /* Append one token per sequence: d_k, d_v are dtype[batch][kv_heads]
- * [head_dim].  The value is quantized at once; the key goes to tail slot
- * n mod G, and when that fills the tail (n+1 a multiple of G) the G tail
- * keys are quantized as key group n/G in the same launch.  Sets n = n + 1.
+ * [head_dim].  R = 0: the value is quantized at once; the key goes to tail
+ * slot n mod G, and when that fills the tail (n+1 a multiple of G) the G
+ * tail keys are quantized as key group n/G in the same launch.  R > 0: key
+ * and value go to ring slot n mod (R+G); when n+1-R reaches a positive
+ * multiple of G, the G-block b = (n+1-R)/G - 1 leaves the window and its
+ * keys (group b) and values (tokens bG .. bG+G-1) are quantized from the
+ * rings in the same launch.  Sets n = n + 1.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_CAPACITY (n == max_tokens), KVQ_ERR_HIP. */
 int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v,
                      void* stream);

@@ -46,6 +46,7 @@ class KvqConfig(ctypes.Structure):
         ("value_bits", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("rope_base", ctypes.c_float),
+        ("residual", ctypes.c_int32),
     ]
 
 
@@ -56,6 +57,7 @@ class KvqLayout(ctypes.Structure):
         ("v_codes", ctypes.c_size_t),
         ("v_meta", ctypes.c_size_t),
         ("k_tail", ctypes.c_size_t),
+        ("v_tail", ctypes.c_size_t),
         ("rope_group", ctypes.c_size_t),
         ("rope_offset", ctypes.c_size_t),
         ("partials", ctypes.c_size_t),
@@ -63,6 +65,7 @@ class KvqLayout(ctypes.Structure):
         ("gcap", ctypes.c_int32),
         ("tcap", ctypes.c_int32),
         ("max_splits", ctypes.c_int32),
+        ("tail_slots", ctypes.c_int32),
     ]
 
 

@@ -328,22 +328,19 @@ __device__ __forceinline__ void load_step(
     load_values<D, KB, VB, QPK, (S::GPW > 1)>(hp, lane, gb * G, g1 * G - 1, sd.vw, sd.vm);
 }
 
-// Softmax update for one wave step and accumulation of its value tokens.
-// Lane `lane` holds score s[h] of token tt = lane (head_dim 64) or lane & 31
-// (head_dim 128), i.e. token t_base + tt; tokens at or past t_end are absent
-// (their value words may be anything: their weight is exactly 0).
+// Online-softmax update for one wave step.  Lane `lane` holds score s[h] of
+// token tt = lane (head_dim 64) or lane & 31 (head_dim 128), i.e. token
+// t_base + tt; tokens at or past t_end are absent and weigh exactly 0.
+// Returns in pw[h] the weight of the lane's own token.
 template <int D, int KB, int VB, int QPK>
-__device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
-                                               const float (&s)[QPK], const uint32_t* vwords,
-                                               const uint32_t* vmetas,
-                                               WaveState<QPK, Shape<D, KB, VB, QPK>::NCL>& st)
+__device__ __forceinline__ void softmax_weights(int lane, int t_base, int t_end,
+                                                const float (&s)[QPK], float (&pw)[QPK],
+                                                WaveState<QPK, Shape<D, KB, VB, QPK>::NCL>& st)
 {
     using S = Shape<D, KB, VB, QPK>;
-    using C = Codec<VB>;
     const int tt_own = (S::NP == 64) ? (lane & 31) : lane;
     const bool own_valid = t_base + tt_own < t_end;
     const bool counts = (S::NP == 32) || lane < 32;  // head_dim 128: lanes l, l+32 share a token
-    float pw[QPK];
 #pragma unroll
     for (int h = 0; h < QPK; ++h) {
         const float sv = own_valid ? s[h] : -INFINITY;
@@ -362,6 +359,20 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
                 st.o[h][c] *= alpha;
         }
     }
+}
+
+// Softmax update for one wave step and accumulation of its value tokens from
+// their code words (absent tokens' words may be anything: they weigh 0).
+template <int D, int KB, int VB, int QPK>
+__device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
+                                               const float (&s)[QPK], const uint32_t* vwords,
+                                               const uint32_t* vmetas,
+                                               WaveState<QPK, Shape<D, KB, VB, QPK>::NCL>& st)
+{
+    using S = Shape<D, KB, VB, QPK>;
+    using C = Codec<VB>;
+    float pw[QPK];
+    softmax_weights<D, KB, VB, QPK>(lane, t_base, t_end, s, pw, st);
     if constexpr (S::PAIRS) {
         // weights of tokens c and c + 16: lanes of rows 0 and 2 hold token
         // c's, rows 1 and 3 token c + 16's
@@ -435,10 +446,127 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
     }
 }
 
+// N consecutive elements of an fp16 (dtype 0) or fp32 row as floats; N a
+// multiple of 4, the address 8-byte (fp16, N = 4) or 16-byte aligned.
+template <int N>
+__device__ __forceinline__ void load_row(const void* src, int dtype, float (&x)[N])
+{
+    if (dtype == 0) {
+        const uint32_t* w = static_cast<const uint32_t*>(src);
+        uint32_t u[N / 2];
+        if constexpr (N % 8 == 0) {
+#pragma unroll
+            for (int k = 0; k < N / 8; ++k) {
+                const uint4 v = reinterpret_cast<const uint4*>(w)[k];
+                u[4 * k] = v.x;
+                u[4 * k + 1] = v.y;
+                u[4 * k + 2] = v.z;
+                u[4 * k + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < N / 4; ++k) {
+                const uint2 v = reinterpret_cast<const uint2*>(w)[k];
+                u[2 * k] = v.x;
+                u[2 * k + 1] = v.y;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+            x[2 * k] = lo_h(u[k]);
+            x[2 * k + 1] = hi_h(u[k]);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k) {
+            const float4 v = static_cast<const float4*>(src)[k];
+            x[4 * k] = v.x;
+            x[4 * k + 1] = v.y;
+            x[4 * k + 2] = v.z;
+            x[4 * k + 3] = v.w;
+        }
+    }
+}
+
+// Softmax update for one wave step of unquantized values (the residual
+// window): rows[tt] is token t_base + tt's value row (rows of D elements,
+// tokens 0 .. cnt-1 present).  Each lane covers the same (token, channel)
+// pairs as for code words, and adds p * v * 2^(pos-24) to the accumulator
+// of a code at bit position pos of that channel, so the one final rescale by
+// 2^(24-pos) serves both.
+template <int D, int KB, int VB, int QPK>
+__device__ __forceinline__ void softmax_fp_values(int lane, int t_base, int cnt,
+                                                  const float (&s)[QPK], const void* rows,
+                                                  int dtype,
+                                                  WaveState<QPK, Shape<D, KB, VB, QPK>::NCL>& st)
+{
+    using S = Shape<D, KB, VB, QPK>;
+    using C = Codec<VB>;
+    float pw[QPK];
+    softmax_weights<D, KB, VB, QPK>(lane, t_base, t_base + cnt, s, pw, st);
+    const size_t esz = dtype == 0 ? 2 : 4;
+    auto row = [&](int tt, int ch) {  // absent tokens read the last present row
+        return static_cast<const char*>(rows) + ((size_t)min(tt, cnt - 1) * D + ch) * esz;
+    };
+    auto scale = [](int cc) { return 1.0f / (float)(1 << (24 - C::pos(cc % C::TPH))); };
+    if constexpr (S::PAIRS) {
+        const Pair pp = swap16(pw[0]);
+        const int r = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float pt = k ? pp.b : pp.a;
+            float x[G];
+            load_row<G>(row(c + 16 * k, r * G), dtype, x);
+#pragma unroll
+            for (int cc = 0; cc < G; ++cc)
+                st.o[0][cc] = fmaf(pt * scale(cc), x[cc], st.o[0][cc]);
+        }
+    } else if constexpr (S::QUADS) {
+        const int r = lane >> 4, c = lane & 15;
+        const int ch0 = (2 * r + (c >> 3)) * S::NW * S::NC;
+        float pk[QPK][4];
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            const Pair pp = swap16(pw[h]);
+            pk[h][0] = pp.a;
+            pk[h][1] = dpp<kDppRor8>(pp.a);
+            pk[h][2] = pp.b;
+            pk[h][3] = dpp<kDppRor8>(pp.b);
+        }
+        // one token row at a time, added into every head
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            constexpr int NCH = S::NW * S::NC;  // 16 channels
+            float x[NCH];
+            load_row<NCH>(row((k & 1 ? (c ^ 8) : c) + (k & 2 ? 16 : 0), ch0), dtype, x);
+#pragma unroll
+            for (int h = 0; h < QPK; ++h)
+#pragma unroll
+                for (int cc = 0; cc < NCH; ++cc)
+                    st.o[h][cc] = fmaf(pk[h][k] * scale(cc), x[cc], st.o[h][cc]);
+        }
+    } else {
+        const int w = lane % S::WPT, vslot = lane / S::WPT;
+#pragma unroll
+        for (int k = 0; k < S::VTOK; ++k) {
+            const int tt = vslot + k * S::TS;
+            float x[S::NC];
+            load_row<S::NC>(row(tt, w * S::NC), dtype, x);
+#pragma unroll
+            for (int h = 0; h < QPK; ++h) {
+                const float pt = __shfl(pw[h], tt);
+#pragma unroll
+                for (int cc = 0; cc < S::NC; ++cc)
+                    st.o[h][cc] = fmaf(pt * scale(cc), x[cc], st.o[h][cc]);
+            }
+        }
+    }
+}
+
 template <int D, int KB, int VB, int QPK>
 __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Planes p, const void* __restrict__ q,
                                                                 float* __restrict__ out, int n,
-                                                                int splits)
+                                                                int splits, int hgroups)
 {
     using S = Shape<D, KB, VB, QPK>;
     using KC = Codec<KB>;
@@ -452,12 +580,17 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
     const int i = lane % NP, gsub = lane / NP;
     const int split = blockIdx.x;
-    const size_t bh = blockIdx.y;
+    // block y = (sequence, KV head, group of QPK of its query heads)
+    const size_t bh = blockIdx.y / hgroups;
     const int b = (int)(bh / p.hkv), kvh = (int)(bh % p.hkv);
-    const int ngq = n / G, tq = ngq * G, cnt_tail = n - tq;
+    const int head0 = (kvh * hgroups + (int)(blockIdx.y % hgroups)) * QPK;
+    // groups [0, ngq) are quantized; tokens [tq, n) are held verbatim in the
+    // tail rings (keys always, values with a residual window), in chunks of
+    // G tokens taken by the waves of the last split
+    const int tq = quantized_tokens(n, p.residual), ngq = tq / G;
+    const int nchunks = (n - tq + G - 1) / G;
     const int g0 = (int)((long long)split * ngq / splits);
     const int g1 = (int)((long long)(split + 1) * ngq / splits);
-    const bool do_tail = (split == splits - 1) && cnt_tail > 0;
 
     // The first step's words go out before anything else: their HBM latency
     // overlaps the query rotation and the twiddle staging.
@@ -481,7 +614,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         const float scale = kLog2e * rsqrtf((float)D);
 #pragma unroll
         for (int h = 0; h < QPK; ++h) {
-            const size_t qi = ((size_t)(b * p.hq + kvh * QPK + h)) * D + 2 * i;
+            const size_t qi = ((size_t)(b * p.hq + head0 + h)) * D + 2 * i;
             const float2 qq = cmul(make_float2(ldf(q, qi, p.dtype), ldf(q, qi + 1, p.dtype)), rot);
             qc[h] = make_float2(qq.x * scale, -qq.y * scale);
         }
@@ -522,58 +655,6 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     }
     float* red = smem + wave * S::NRED * 64 * RS;
     const int red_half = lane & ~31, red_col = lane & 31;
-
-    if (do_tail && wave == nwaves - 1) {
-        // The tail (cnt_tail < G unquantized keys, slot j = token tq + j) is
-        // scored like one more group by the wave with the fewest groups:
-        // lane = channel pair, the tail tokens across the lane's registers.
-        uint32_t vw[S::NVW], vm[S::NVM];
-        load_values<D, KB, VB, QPK, true>(hp, lane, tq, n - 1, vw, vm);
-        float tx[G], ty[G];
-        const size_t trow = (bh * G) * D + 2 * i;  // element index of (slot 0, channel 2i)
-        if (p.dtype == 0) {
-            const uint32_t* t32 = reinterpret_cast<const uint32_t*>(p.k_tail) + trow / 2;
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const uint32_t w = (gsub == 0 && j < cnt_tail) ? t32[(size_t)j * (D / 2)] : 0u;
-                tx[j] = lo_h(w);
-                ty[j] = hi_h(w);
-            }
-        } else {
-            const float2* t64 = reinterpret_cast<const float2*>(p.k_tail) + trow / 2;
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const float2 w = (gsub == 0 && j < cnt_tail) ? t64[(size_t)j * (D / 2)]
-                                                             : make_float2(0.f, 0.f);
-                tx[j] = w.x;
-                ty[j] = w.y;
-            }
-        }
-        const float2 rg = p.rope_group[(size_t)ngq * NP + i];
-        float s[QPK];
-#pragma unroll
-        for (int h = 0; h < QPK; ++h) {
-            const float2 Q = cmul(qc[h], rg);
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                // Re[T_j Q (x + iy)]; the twiddle carries (T.x, -T.y) * 2^(24-pos)
-                const float vr = Q.x * tx[j] - Q.y * ty[j];
-                const float vi = Q.x * ty[j] + Q.y * tx[j];
-                const float unscale = 1.0f / (float)(1 << (24 - KC::pos(j % KC::TPH)));
-                const float2 tw = twiddle(j);
-                red[lane * RS + j] = fmaf(tw.x, vr, tw.y * vi) * unscale;
-            }
-            float a4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < 32; ++m)
-                a4[m & 3] += red[(red_half + m) * RS + red_col];
-            float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-            if (NP == 64)
-                acc = half_sum(acc);
-            s[h] = acc;
-        }
-        softmax_values<D, KB, VB, QPK>(lane, tq, n, s, vw, vm, st);
-    }
 
     // Waves of a SIMD otherwise run oldest-first, so the oldest finishes its
     // share long before the youngest, which then runs alone at a fraction of
@@ -715,6 +796,68 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
 
     __builtin_amdgcn_s_setprio(0);
 
+    for (int ch = nwaves - 1 - wave; split == splits - 1 && ch < nchunks; ch += nwaves) {
+        asm volatile("" : "+v"(tw_base));  // keep the twiddle reads in the loop
+        // One chunk of unquantized tokens t0 .. t0+cnt-1 (ring rows from
+        // row0, contiguous: the ring and t0 are multiples of G), scored like
+        // one more group after the quantized ones (the softmax is order-free):
+        // lane = channel pair, the tokens across its registers.
+        const int t0 = tq + ch * G, cnt = min(G, n - t0);
+        const size_t row0 = bh * (size_t)p.ring + t0 % p.ring;  // ring row of token t0
+        float tx[G], ty[G];
+        const size_t trow = row0 * D + 2 * i;  // element index of (token t0, channel 2i)
+        if (p.dtype == 0) {
+            const uint32_t* t32 = reinterpret_cast<const uint32_t*>(p.k_tail) + trow / 2;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const uint32_t w = (gsub == 0 && j < cnt) ? t32[(size_t)j * (D / 2)] : 0u;
+                tx[j] = lo_h(w);
+                ty[j] = hi_h(w);
+            }
+        } else {
+            const float2* t64 = reinterpret_cast<const float2*>(p.k_tail) + trow / 2;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float2 w = (gsub == 0 && j < cnt) ? t64[(size_t)j * (D / 2)]
+                                                        : make_float2(0.f, 0.f);
+                tx[j] = w.x;
+                ty[j] = w.y;
+            }
+        }
+        const float2 rg = p.rope_group[(size_t)(t0 / G) * NP + i];
+        float s[QPK];
+#pragma unroll
+        for (int h = 0; h < QPK; ++h) {
+            const float2 Q = cmul(qc[h], rg);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                // Re[T_j Q (x + iy)]; the twiddle carries (T.x, -T.y) * 2^(24-pos)
+                const float vr = Q.x * tx[j] - Q.y * ty[j];
+                const float vi = Q.x * ty[j] + Q.y * tx[j];
+                const float unscale = 1.0f / (float)(1 << (24 - KC::pos(j % KC::TPH)));
+                const float2 tw = twiddle(j);
+                red[lane * RS + j] = fmaf(tw.x, vr, tw.y * vi) * unscale;
+            }
+            float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 32; ++m)
+                a4[m & 3] += red[(red_half + m) * RS + red_col];
+            float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+            if (NP == 64)
+                acc = half_sum(acc);
+            s[h] = acc;
+        }
+        if (p.residual > 0) {
+            const char* vrows = static_cast<const char*>(p.v_tail) +
+                                row0 * D * (p.dtype == 0 ? 2 : 4);
+            softmax_fp_values<D, KB, VB, QPK>(lane, t0, cnt, s, vrows, p.dtype, st);
+        } else {
+            uint32_t vw[S::NVW], vm[S::NVM];
+            load_values<D, KB, VB, QPK, true>(hp, lane, t0, n - 1, vw, vm);
+            softmax_values<D, KB, VB, QPK>(lane, t0, n, s, vw, vm, st);
+        }
+    }
+
     // ---- merge the waves of this block
     __syncthreads();  // every wave is done with its reduce buffer
     float* sm = smem;                           // [nwaves][QPK]
@@ -805,7 +948,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 acc += f * so[(w * QPK + h) * D + c];
             }
         }
-        const size_t row = (size_t)b * p.hq + kvh * QPK + h;
+        const size_t row = (size_t)b * p.hq + head0 + h;
         if (single) {
             out[row * D + c] = acc / L;
         } else {
@@ -859,10 +1002,11 @@ template <int D, int KB, int VB, int QPK>
 void launch(const Planes& p, const void* q, float* out, int n, int splits, int nwaves,
             hipStream_t stream)
 {
-    dim3 grid(splits, p.nb * p.hkv);
+    const int hgroups = p.hq / p.hkv / QPK;
+    dim3 grid(splits, p.nb * p.hkv * hgroups);
     nwaves = nwaves < max_block_waves(QPK) ? nwaves : max_block_waves(QPK);
     attend_kernel<D, KB, VB, QPK><<<grid, 64 * nwaves, attend_lds_bytes<D, KB, VB, QPK>(nwaves),
-                                    stream>>>(p, q, out, n, splits);
+                                    stream>>>(p, q, out, n, splits, hgroups);
     if (splits > 1)
         combine_kernel<D><<<p.nb * p.hq, D, 0, stream>>>(p.partials, p.max_splits, splits, out);
 }
@@ -874,8 +1018,8 @@ void by_qpk(const Planes& p, const void* q, float* out, int n, int splits, int n
     switch (p.hq / p.hkv) {
     case 1: launch<D, KB, VB, 1>(p, q, out, n, splits, nwaves, s); break;
     case 2: launch<D, KB, VB, 2>(p, q, out, n, splits, nwaves, s); break;
-    case 4: launch<D, KB, VB, 4>(p, q, out, n, splits, nwaves, s); break;
-    case 8: launch<D, KB, VB, 8>(p, q, out, n, splits, nwaves, s); break;
+    case 4:  // 8 query heads per KV head run as two groups of 4 (registers)
+    case 8: launch<D, KB, VB, 4>(p, q, out, n, splits, nwaves, s); break;
     }
 }
 

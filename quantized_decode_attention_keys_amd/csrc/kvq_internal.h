@@ -14,18 +14,33 @@ constexpr int kGroup = 32;  // G: tokens per key group, channels per value group
 // query head per KV head, 8 (up to 256) when several query heads share one.
 constexpr int max_block_waves(int qpk) { return qpk == 1 ? 16 : 8; }
 
+// Query heads per attention block: at most 4; 8 query heads per KV head run
+// as two blocks of 4 over the same KV head.
+constexpr int block_heads(int qpk) { return qpk < 4 ? qpk : 4; }
+
 // Everything a kernel needs to address the planes of one cache.
 struct Planes {
     uint32_t* k_codes;   // [nb][hkv][gcap][D][wk]
     uint32_t* k_meta;    // [nb][hkv][gcap][D]
     uint32_t* v_codes;   // [nb][hkv][tcap][D/G][wv]
     uint32_t* v_meta;    // [nb][hkv][tcap][D/G]
-    void* k_tail;        // dtype[nb][hkv][G][D]
+    void* k_tail;        // dtype[nb][hkv][ring][D]: key t >= Tq in slot t mod ring
+    void* v_tail;        // dtype[nb][hkv][ring][D]: the same for values (residual > 0)
     const float2* rope_group;   // [gcap][D/2]  (cos, sin) of g*G*theta_i
     const float2* rope_offset;  // [G][D/2]     (cos, sin) of j*theta_i
     float* partials;     // [nb*hq][max_splits][D+2]
     int nb, hq, hkv, D, kbits, vbits, gcap, tcap, max_splits, dtype;
+    int residual, ring;  // R and R + G
 };
+
+// Tq: tokens [0, Tq) of an n-token cache are quantized (keys in whole
+// groups); the keys of [Tq, n), and with a residual window its values, are
+// held verbatim in the tail rings.
+__host__ __device__ inline int quantized_tokens(int n, int residual)
+{
+    const int a = n - residual;
+    return a > 0 ? a / kGroup * kGroup : 0;
+}
 
 // Launch wrappers (kvq_kernels.hip).  All enqueue on `stream` and return the
 // hipGetLastError() status of the launches.

@@ -63,10 +63,11 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(Planes p, const T* __re
     p.k_meta[gc] = meta;
 }
 
-// Copy the last n_tokens mod G keys of each sequence/head into the tail.
+// Copy tokens [tq, n_tokens) of each sequence/head verbatim into a tail
+// ring (token t in slot t mod ring).
 template <typename T>
-__global__ void copy_tail_kernel(Planes p, const T* __restrict__ k, int n_tokens, int tq,
-                                 size_t total)
+__global__ void copy_tail_kernel(Planes p, const T* __restrict__ src, T* __restrict__ ring,
+                                 int n_tokens, int tq, size_t total)
 {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total)
@@ -74,18 +75,19 @@ __global__ void copy_tail_kernel(Planes p, const T* __restrict__ k, int n_tokens
     const int D = p.D;
     const int rem = n_tokens - tq;
     const int c = idx % D;
-    const int j = (idx / D) % rem;
+    const int t = tq + (int)((idx / D) % rem);
     const size_t bh = idx / ((size_t)D * rem);
-    T* tail = reinterpret_cast<T*>(p.k_tail);
-    tail[(bh * G + j) * D + c] = k[(bh * n_tokens + tq + j) * D + c];
+    ring[(bh * p.ring + t % p.ring) * D + c] = src[(bh * n_tokens + t) * D + c];
 }
 
 // One thread per (sequence*head, token, channel group): the group is G
 // consecutive channels of one token row (64 contiguous bytes at fp16).
-// Input tokens [0, n_src) go to cache slots [t_dst0, t_dst0 + n_src).
+// Input tokens [0, n_src) of rows of src_stride tokens go to cache slots
+// [t_dst0, t_dst0 + n_src).
 template <typename T, int BITS>
 __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __restrict__ v,
-                                                           int n_src, int t_dst0, size_t total)
+                                                           int n_src, int src_stride, int t_dst0,
+                                                           size_t total)
 {
     constexpr int WV = G * BITS / 32;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __
     const size_t r = idx / ncg;
     const int t = r % n_src;
     const size_t bh = r / n_src;
-    const T* src = v + (bh * n_src + t) * D + (size_t)cg * G;
+    const T* src = v + (bh * src_stride + t) * D + (size_t)cg * G;
     float x[G];
 #pragma unroll
     for (int j = 0; j < G; ++j)
@@ -152,16 +154,16 @@ __global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __rest
         if (j == 0)
             p.v_meta[tc] = gp.meta;
     }
-    T* tail = reinterpret_cast<T*>(p.k_tail);
+    T* tail = reinterpret_cast<T*>(p.k_tail) + bh * p.ring * D;  // ring of G slots
     const int slot = n % G;
     const T val = k[bh * D + c];
-    tail[(bh * G + slot) * D + c] = val;
+    tail[slot * D + c] = val;
     if (slot != G - 1)
         return;
     float x[G];
 #pragma unroll
     for (int j = 0; j < G - 1; ++j)
-        x[j] = to_f32(tail[(bh * G + j) * D + c]);
+        x[j] = to_f32(tail[j * D + c]);
     x[G - 1] = to_f32(val);
     uint32_t w[WK];
     const uint32_t meta = quantize_group<KBITS>(x, w);
@@ -173,14 +175,71 @@ __global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __rest
     p.k_meta[gc] = meta;
 }
 
+// Append with a residual window (R > 0): key and value of token n go to ring
+// slot n mod (R+G).  When n+1-R reaches a positive multiple of G, block b =
+// (n+1-R)/G - 1 (tokens bG .. bG+G-1, all older than the window) is quantized
+// from the rings in the same launch: thread c codes key channel c of the
+// block (one key group) and value group c of the block (token bG + c/(D/G),
+// channel group c mod (D/G)).  The block's slots differ from slot n mod (R+G)
+// (they are R .. R+G-1 tokens older), so no thread reads what another writes.
+template <typename T, int KBITS, int VBITS>
+__global__ void append_residual_kernel(Planes p, const T* __restrict__ k,
+                                       const T* __restrict__ v, int n)
+{
+    constexpr int WK = G * KBITS / 32, WV = G * VBITS / 32;
+    const int D = p.D;
+    const int c = threadIdx.x;
+    const size_t bh = blockIdx.x;
+    if (c >= D)
+        return;
+    T* kring = reinterpret_cast<T*>(p.k_tail) + bh * p.ring * D;
+    T* vring = reinterpret_cast<T*>(p.v_tail) + bh * p.ring * D;
+    const int slot = n % p.ring;
+    kring[slot * D + c] = k[bh * D + c];
+    vring[slot * D + c] = v[bh * D + c];
+    const int aged = n + 1 - p.residual;
+    if (aged < G || aged % G != 0)
+        return;
+    const int b = aged / G - 1;
+    {
+        float x[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            x[j] = to_f32(kring[((b * G + j) % p.ring) * D + c]);
+        uint32_t w[WK];
+        const uint32_t meta = quantize_group<KBITS>(x, w);
+        const size_t gc = (bh * p.gcap + b) * D + c;
+#pragma unroll
+        for (int i = 0; i < WK; ++i)
+            p.k_codes[gc * WK + i] = w[i];
+        p.k_meta[gc] = meta;
+    }
+    {
+        const int ncg = D / G;
+        const int t = b * G + c / ncg, cg = c % ncg;
+        const T* src = vring + (size_t)(t % p.ring) * D + cg * G;
+        float x[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            x[j] = to_f32(src[j]);
+        uint32_t w[WV];
+        const uint32_t meta = quantize_group<VBITS>(x, w);
+        const size_t tc = (bh * p.tcap + t) * ncg + cg;
+#pragma unroll
+        for (int i = 0; i < WV; ++i)
+            p.v_codes[tc * WV + i] = w[i];
+        p.v_meta[tc] = meta;
+    }
+}
+
 // ------------------------------------------------------------- dispatch --
 
 template <typename T>
 hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tokens,
                               hipStream_t stream)
 {
-    const int ngroups = n_tokens / G;
-    const int tq = ngroups * G;
+    const int tq = quantized_tokens(n_tokens, p.residual);
+    const int ngroups = tq / G;
     const int nbh = p.nb * p.hkv;
     if (ngroups > 0) {
         const int gpb = 256 / p.D;
@@ -191,16 +250,25 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
         case 8: quant_keys_kernel<T, 8><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, ngroups); break;
         }
     }
-    if (n_tokens > tq) {
-        const size_t total = (size_t)nbh * (n_tokens - tq) * p.D;
-        copy_tail_kernel<T><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p, k, n_tokens, tq, total);
-    }
-    const size_t vg = (size_t)nbh * n_tokens * (p.D / G);
+    const size_t rest = (size_t)nbh * (n_tokens - tq) * p.D;
+    const unsigned rblocks = (unsigned)((rest + 255) / 256);
+    if (rest > 0)
+        copy_tail_kernel<T><<<rblocks, 256, 0, stream>>>(p, k, static_cast<T*>(p.k_tail), n_tokens,
+                                                         tq, rest);
+    // values: all quantized without a window; with one, [0, tq) quantized
+    // and the rest copied to the value ring
+    const int vq = p.residual > 0 ? tq : n_tokens;
+    if (p.residual > 0 && rest > 0)
+        copy_tail_kernel<T><<<rblocks, 256, 0, stream>>>(p, v, static_cast<T*>(p.v_tail), n_tokens,
+                                                         tq, rest);
+    const size_t vg = (size_t)nbh * vq * (p.D / G);
     const unsigned vblocks = (unsigned)((vg + 255) / 256);
-    switch (p.vbits) {
-    case 2: quant_values_kernel<T, 2><<<vblocks, 256, 0, stream>>>(p, v, n_tokens, 0, vg); break;
-    case 4: quant_values_kernel<T, 4><<<vblocks, 256, 0, stream>>>(p, v, n_tokens, 0, vg); break;
-    case 8: quant_values_kernel<T, 8><<<vblocks, 256, 0, stream>>>(p, v, n_tokens, 0, vg); break;
+    if (vg > 0) {
+        switch (p.vbits) {
+        case 2: quant_values_kernel<T, 2><<<vblocks, 256, 0, stream>>>(p, v, vq, n_tokens, 0, vg); break;
+        case 4: quant_values_kernel<T, 4><<<vblocks, 256, 0, stream>>>(p, v, vq, n_tokens, 0, vg); break;
+        case 8: quant_values_kernel<T, 8><<<vblocks, 256, 0, stream>>>(p, v, vq, n_tokens, 0, vg); break;
+        }
     }
     return hipGetLastError();
 }
@@ -209,6 +277,14 @@ template <typename T, int KBITS>
 void append_kb(const Planes& p, const T* k, const T* v, int n, hipStream_t stream)
 {
     const int nbh = p.nb * p.hkv;
+    if (p.residual > 0) {
+        switch (p.vbits) {
+        case 2: append_residual_kernel<T, KBITS, 2><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+        case 4: append_residual_kernel<T, KBITS, 4><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+        case 8: append_residual_kernel<T, KBITS, 8><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+        }
+        return;
+    }
     switch (p.vbits) {
     case 2: append_kernel<T, KBITS, 2><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
     case 4: append_kernel<T, KBITS, 4><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;

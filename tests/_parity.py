@@ -20,10 +20,10 @@ def to_gpu(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
 
 
-def make_cache(cfg, max_tokens):
+def make_cache(cfg, max_tokens, residual=0):
     return QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
                             cfg.key_bits, cfg.value_bits, _TORCH[cfg.np_dtype],
-                            rope_base=cfg.rope_base, device=dev())
+                            rope_base=cfg.rope_base, device=dev(), residual=residual)
 
 
 def gpu_planes(cache):
@@ -35,25 +35,39 @@ def gpu_planes(cache):
     return out
 
 
-def oracle_planes(cfg, k, v, max_tokens):
-    kc, km, kt = oracle.quantize_keys(k, cfg.key_bits, cfg.group, max_tokens=max_tokens)
-    vc, vm = oracle.quantize_values(v, cfg.value_bits, cfg.group, max_tokens=max_tokens)
-    return dict(k_codes=kc, k_meta=km, k_tail=kt, v_codes=vc, v_meta=vm)
+def oracle_planes(cfg, k, v, max_tokens, residual=0):
+    kc, km, kt = oracle.quantize_keys(k, cfg.key_bits, cfg.group, max_tokens=max_tokens,
+                                      residual=residual)
+    vals = oracle.quantize_values(v, cfg.value_bits, cfg.group, max_tokens=max_tokens,
+                                  residual=residual)
+    pl = dict(k_codes=kc, k_meta=km, k_tail=kt, v_codes=vals[0], v_meta=vals[1])
+    if residual > 0:
+        pl["v_tail"] = vals[2]
+    return pl
 
 
-def assert_planes_equal(gp, op, n, G=32, seqs=None):
-    """Bit-exact comparison of every slot that holds data at length n."""
-    ng, tq = n // G, (n // G) * G
+def assert_planes_equal(gp, op, n, G=32, seqs=None, residual=0):
+    """Bit-exact comparison of every slot that holds data at length n: codes
+    and metadata of the quantized tokens, ring slots of the others."""
+    tq = oracle.quantized_tokens(n, G, residual)
+    vq = tq if residual > 0 else n
+    ring = residual + G
+    # seqs selects GPU sequences; op holds the oracle planes of just those
     sel = slice(None) if seqs is None else list(seqs)
     g = {k: a[sel] for k, a in gp.items()}
-    for name, lim in (("k_codes", ng), ("k_meta", ng), ("v_codes", n), ("v_meta", n)):
-        a, b = g[name][:, :, :lim], op[name][:, :, :lim]
+    o = op
+    for name, lim in (("k_codes", tq // G), ("k_meta", tq // G), ("v_codes", vq),
+                      ("v_meta", vq)):
+        a, b = g[name][:, :, :lim], o[name][:, :, :lim]
         if not np.array_equal(a, b):
             bad = np.argwhere(a != b)
             raise AssertionError(f"{name}: {len(bad)} mismatches, first at {bad[0].tolist()}: "
                                  f"gpu {a[tuple(bad[0])]:#x} oracle {b[tuple(bad[0])]:#x}")
-    at, bt = g["k_tail"][:, :, :n - tq], op["k_tail"][:, :, :n - tq]
-    assert np.array_equal(at.view(np.uint8), bt.view(np.uint8)), "k_tail differs"
+    slots = [t % ring for t in range(tq, n)]
+    tails = ("k_tail", "v_tail") if residual > 0 else ("k_tail",)
+    for name in tails:
+        at, bt = g[name][:, :, slots], o[name][:, :, slots]
+        assert np.array_equal(at.view(np.uint8), bt.view(np.uint8)), f"{name} differs"
 
 
 def assert_attention_close(out, ref, tol=TOL):
