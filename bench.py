@@ -71,16 +71,26 @@ def calibrate_copy():
     print(json.dumps({"calibration_copy_bytes": x.numel() * 4, "copies": 3}))
 
 
-def attend_bytes(cfg, n: int) -> int:
+def quantized_tokens(n: int, G: int, residual: int) -> int:
+    """Tokens [0, Tq) are quantized; with a residual window R the last
+    tokens (at least R) stay in full precision."""
+    a = n - residual
+    return a // G * G if a > 0 else 0
+
+
+def attend_bytes(cfg, n: int, residual: int = 0) -> int:
     """Algorithmic bytes of one decode-attention call at length n: packed key
-    codes + key meta + key tail + value codes + value meta + q + out."""
+    codes + key meta + unquantized keys + value codes + value meta (+
+    unquantized values with a residual window) + q + out."""
     G, D = cfg.group, cfg.head_dim
     nbh = cfg.batch * cfg.kv_heads
     esz = 2 if cfg.dtype == "float16" else 4
-    tq = n // G * G
+    tq = quantized_tokens(n, G, residual)
+    vq = tq if residual > 0 else n
     return (nbh * tq * D * cfg.key_bits // 8 + nbh * (tq // G) * D * 4
             + nbh * (n - tq) * D * esz
-            + nbh * n * D * cfg.value_bits // 8 + nbh * n * (D // G) * 4
+            + nbh * vq * D * cfg.value_bits // 8 + nbh * vq * (D // G) * 4
+            + nbh * (n - vq) * D * esz
             + cfg.batch * cfg.q_heads * D * esz + cfg.batch * cfg.q_heads * D * 4)
 
 
@@ -93,16 +103,18 @@ def attend_flops(cfg, n: int) -> int:
     return cfg.batch * cfg.kv_heads * n * cfg.head_dim * (7 + 4 * qpk)
 
 
-def prefill_bytes(cfg, n: int) -> int:
+def prefill_bytes(cfg, n: int, residual: int = 0) -> int:
     """Quantize-and-pack of n tokens: K and V read once, planes written."""
     G, D = cfg.group, cfg.head_dim
     nbh = cfg.batch * cfg.kv_heads
     esz = 2 if cfg.dtype == "float16" else 4
-    tq = n // G * G
+    tq = quantized_tokens(n, G, residual)
+    vq = tq if residual > 0 else n
     return (2 * nbh * n * D * esz
             + nbh * tq * D * cfg.key_bits // 8 + nbh * (tq // G) * D * 4
             + nbh * (n - tq) * D * esz
-            + nbh * n * D * cfg.value_bits // 8 + nbh * n * (D // G) * 4)
+            + nbh * vq * D * cfg.value_bits // 8 + nbh * vq * (D // G) * 4
+            + nbh * (n - vq) * D * esz)
 
 
 class HipEvents:
@@ -143,7 +155,7 @@ class HipEvents:
         self.ev = []
 
 
-def cpu_baseline(cfg, n: int, budget_s: float = 12.0):
+def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0):
     """The oracle (plain single-threaded fp64 C) on a bounded sample of the
     same workload: decode attention for whole sequences, rows timed until
     about budget_s seconds of CPU work."""
@@ -158,17 +170,19 @@ def cpu_baseline(cfg, n: int, budget_s: float = 12.0):
     q = synth.make_query(cfg, 0, 0)
     rows_done, t_total, bytes_done = 0, 0.0, 0
     one = synth.scaled(cfg, batch=1)
-    per_row = attend_bytes(one, n) / cfg.q_heads
+    per_row = attend_bytes(one, n, residual) / cfg.q_heads
     for b in range(cfg.batch):
         k = synth.make_keys(cfg, 0, 0, n, seqs=[b])
         v = synth.make_values(cfg, 0, 0, n, seqs=[b])
-        kc, km, kt = oracle.quantize_keys(k, cfg.key_bits, cfg.group)
-        vc, vm = oracle.quantize_values(v, cfg.value_bits, cfg.group)
-        pl = dict(k_codes=kc, k_meta=km, k_tail=kt, v_codes=vc, v_meta=vm)
+        kc, km, kt = oracle.quantize_keys(k, cfg.key_bits, cfg.group, residual=residual)
+        vals = oracle.quantize_values(v, cfg.value_bits, cfg.group, residual=residual)
+        pl = dict(k_codes=kc, k_meta=km, k_tail=kt, v_codes=vals[0], v_meta=vals[1])
+        if residual > 0:
+            pl["v_tail"] = vals[2]
         for r in range(cfg.q_heads):
             t0 = time.perf_counter()
             oracle.attend(pl, q[b:b + 1], n, cfg.key_bits, cfg.value_bits, cfg.kv_heads,
-                          cfg.group, cfg.rope_base, rows=(r, r + 1))
+                          cfg.group, cfg.rope_base, rows=(r, r + 1), residual=residual)
             t_total += time.perf_counter() - t0
             rows_done += 1
             bytes_done += per_row
@@ -196,6 +210,8 @@ def main():
     ap.add_argument("--config", default="llama2_7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--caches", type=int, default=0, help="rotating caches (0 = auto)")
+    ap.add_argument("--residual", type=int, default=0,
+                    help="recent tokens kept in full precision (a multiple of 32)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
@@ -223,7 +239,8 @@ def main():
     tdt = torch.float16 if cfg.dtype == "float16" else torch.float32
     total_steps = args.warmup + args.steps
 
-    cache_bytes = attend_bytes(cfg, n)
+    Rw = args.residual
+    cache_bytes = attend_bytes(cfg, n, Rw)
     R = args.caches or max(2, math.ceil(2 * INFINITY_CACHE / cache_bytes) + 1)
     visits = math.ceil(total_steps / R)
     max_tokens = n + visits
@@ -239,7 +256,8 @@ def main():
     out = torch.empty((cfg.batch, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
 
     caches = [QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
-                               cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev)
+                               cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev,
+                               residual=Rw)
               for _ in range(R)]
     # prefill (quantize-and-pack of the whole prompt), timed per cache after
     # one untimed prefill of a one-group cache (first launches load the code)
@@ -304,7 +322,7 @@ def main():
         raise RuntimeError("cache lengths do not match the steps issued")
 
     wall = t1 - t0
-    total_bytes = sum(attend_bytes(cfg, L) for L in lengths)
+    total_bytes = sum(attend_bytes(cfg, L, Rw) for L in lengths)
     value = total_bytes / wall / 1e9
     attend_ms = np.array([hev.elapsed_ms(2 * j, 2 * j + 1) for j in range(args.steps)])
     hev.close()
@@ -332,6 +350,7 @@ def main():
             "batch": cfg.batch, "q_heads": cfg.q_heads, "kv_heads": cfg.kv_heads,
             "head_dim": cfg.head_dim, "context": n, "key_bits": cfg.key_bits,
             "value_bits": cfg.value_bits, "group": cfg.group, "kv_dtype": cfg.dtype,
+            "residual": Rw,
             "context_during_steps": [min(lengths), max(lengths)],
             "rotating_caches": R,
             "parallelism": "single GPU",
@@ -344,7 +363,7 @@ def main():
             "peak": FP32_VECTOR_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(cfg.name),
+            "traffic": measured_traffic(cfg.name) if Rw == 0 else None,
             "kernel": "attend_kernel (decode attention); HIP events around each "
                       "kvq_attend_decode call in the timed loop",
             "flops_per_launch": int(flops_per_launch),
@@ -358,14 +377,14 @@ def main():
         "prefill": {
             "tokens": n - 1,
             "median_ms": round(float(np.median(pf_ms)), 4),
-            "GB_per_s": round(prefill_bytes(cfg, n - 1) / (np.median(pf_ms) / 1e3) / 1e9, 2),
+            "GB_per_s": round(prefill_bytes(cfg, n - 1, Rw) / (np.median(pf_ms) / 1e3) / 1e9, 2),
             "tokens_per_s": round(cfg.batch * (n - 1) / (np.median(pf_ms) / 1e3), 1),
         },
     }
     for c in caches:
         c.close()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, n)
+        res["cpu_baseline"] = cpu_baseline(cfg, n, residual=Rw)
     print(json.dumps(res), flush=True)
 
 
