@@ -61,14 +61,16 @@ def lib() -> ctypes.CDLL:
         L.orc_code_at.restype = i
         L.orc_quantized_tokens.argtypes = [i, i, i]
         L.orc_quantized_tokens.restype = i
-        L.orc_quantize_keys.argtypes = [P, i, i, i, i, i, i, i, i, i, P, P, P]
+        L.orc_quantized_end.argtypes = [i, i, i, i]
+        L.orc_quantized_end.restype = i
+        L.orc_quantize_keys.argtypes = [P, i, i, i, i, i, i, i, i, i, i, P, P, P, P]
         L.orc_quantize_keys.restype = i
-        L.orc_quantize_values.argtypes = [P, i, i, i, i, i, i, i, i, i, P, P, P]
+        L.orc_quantize_values.argtypes = [P, i, i, i, i, i, i, i, i, i, i, P, P, P, P]
         L.orc_quantize_values.restype = i
         L.orc_rope.argtypes = [P, i, d, d]
         L.orc_rope.restype = None
-        L.orc_attend.argtypes = [i, i, i, i, i, i, i, i, i, i, d, P, P, P, P, P,
-                                 P, i, P, i, i, i, P]
+        L.orc_attend.argtypes = [i, i, i, i, i, i, i, i, i, i, i, d, P, P, P, P, P,
+                                 P, P, P, i, P, i, i, i, P]
         L.orc_attend.restype = i
         L.orc_attend_dense.argtypes = [i, i, i, i, d, P, P, i, P, i, i, i, P]
         L.orc_attend_dense.restype = i
@@ -127,12 +129,13 @@ def unpack(words, n: int, bits: int) -> np.ndarray:
     return codes
 
 
-def quantized_tokens(n: int, G: int = 32, residual: int = 0) -> int:
-    """Tq: tokens [0, Tq) are quantized, [Tq, n) held in full precision."""
-    return lib().orc_quantized_tokens(n, G, residual)
+def quantized_tokens(n: int, G: int = 32, residual: int = 0, sink: int = 0) -> int:
+    """Tq: tokens [min(n, sink), Tq) are quantized, the sink tokens and
+    [Tq, n) held in full precision."""
+    return lib().orc_quantized_end(n, G, residual, sink)
 
 
-def plane_shapes(nb, hkv, D, G, kbits, vbits, max_tokens, residual=0):
+def plane_shapes(nb, hkv, D, G, kbits, vbits, max_tokens, residual=0, sink=0):
     """Shapes of the packed planes for a cache of capacity max_tokens.  The
     key tail (and with residual > 0 the value tail) is a ring of
     residual + G token slots."""
@@ -146,42 +149,55 @@ def plane_shapes(nb, hkv, D, G, kbits, vbits, max_tokens, residual=0):
         "v_meta": (nb, hkv, tcap, D // G),
         "k_tail": (nb, hkv, ring, D),
         "v_tail": (nb, hkv, ring if residual > 0 else 0, D),
+        "k_sink": (nb, hkv, sink, D),
+        "v_sink": (nb, hkv, sink, D),
     }
 
 
-def quantize_keys(k: np.ndarray, bits: int, G: int = 32, max_tokens=None, residual=0):
-    """Key planes for k[nb][Hkv][T][D]: (k_codes, k_meta, k_tail)."""
+def quantize_keys(k: np.ndarray, bits: int, G: int = 32, max_tokens=None, residual=0,
+                  sink=0):
+    """Key planes for k[nb][Hkv][T][D]: (k_codes, k_meta, k_tail), and the
+    key sink fourth when sink > 0."""
     k = np.ascontiguousarray(k)
     nb, hkv, T, D = k.shape
     cap = T if max_tokens is None else max_tokens
-    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1), residual)
+    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1), residual, sink)
     kc = np.zeros(sh["k_codes"], dtype=np.uint32)
     km = np.zeros(sh["k_meta"], dtype=np.uint32)
     kt = np.zeros(sh["k_tail"], dtype=k.dtype)
+    ks = np.zeros(sh["k_sink"], dtype=k.dtype)
     rc = lib().orc_quantize_keys(_ptr(k), _dtype_code(k), nb, hkv, T, D, G,
-                                 bits, residual, sh["k_meta"][2], _ptr(kc), _ptr(km),
-                                 _ptr(kt))
+                                 bits, residual, sink, sh["k_meta"][2], _ptr(kc), _ptr(km),
+                                 _ptr(kt), _ptr(ks) if sink > 0 else None)
     if rc != 0:
         raise ValueError("orc_quantize_keys failed")
-    return kc, km, kt
+    return (kc, km, kt, ks) if sink > 0 else (kc, km, kt)
 
 
-def quantize_values(v: np.ndarray, bits: int, G: int = 32, max_tokens=None, residual=0):
-    """Value planes for v[nb][Hkv][T][D]: (v_codes, v_meta), and the value
-    tail ring third when residual > 0."""
+def quantize_values(v: np.ndarray, bits: int, G: int = 32, max_tokens=None, residual=0,
+                    sink=0):
+    """Value planes for v[nb][Hkv][T][D]: (v_codes, v_meta), then the value
+    tail ring when residual > 0, then the value sink when sink > 0."""
     v = np.ascontiguousarray(v)
     nb, hkv, T, D = v.shape
     cap = T if max_tokens is None else max_tokens
-    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1), residual)
+    sh = plane_shapes(nb, hkv, D, G, bits, bits, max(cap, 1), residual, sink)
     vc = np.zeros(sh["v_codes"], dtype=np.uint32)
     vm = np.zeros(sh["v_meta"], dtype=np.uint32)
     vt = np.zeros(sh["v_tail"], dtype=v.dtype)
+    vs = np.zeros(sh["v_sink"], dtype=v.dtype)
     rc = lib().orc_quantize_values(_ptr(v), _dtype_code(v), nb, hkv, T, D, G,
-                                   bits, residual, sh["v_meta"][2], _ptr(vc), _ptr(vm),
-                                   _ptr(vt) if residual > 0 else None)
+                                   bits, residual, sink, sh["v_meta"][2], _ptr(vc), _ptr(vm),
+                                   _ptr(vt) if residual > 0 else None,
+                                   _ptr(vs) if sink > 0 else None)
     if rc != 0:
         raise ValueError("orc_quantize_values failed")
-    return (vc, vm, vt) if residual > 0 else (vc, vm)
+    out = (vc, vm)
+    if residual > 0:
+        out += (vt,)
+    if sink > 0:
+        out += (vs,)
+    return out
 
 
 # ---------------------------------------------------------------- attention
@@ -194,11 +210,11 @@ def rope(u, p: float, base: float = 10000.0) -> np.ndarray:
 
 def attend(planes: dict, q: np.ndarray, n: int, kbits: int, vbits: int,
            hkv: int, G: int = 32, base: float = 10000.0, rows=None,
-           residual: int = 0) -> np.ndarray:
+           residual: int = 0, sink: int = 0) -> np.ndarray:
     """Decode attention over quantized planes for queries q[nb][Hq][D].
 
-    ``planes`` holds k_codes, k_meta, k_tail, v_codes, v_meta (numpy), and
-    v_tail when residual > 0.  The tails' element type is q's.  ``rows`` =
+    ``planes`` holds k_codes, k_meta, k_tail, v_codes, v_meta (numpy), v_tail
+    when residual > 0, k_sink and v_sink when sink > 0.  The tails' element type is q's.  ``rows`` =
     (begin, end) over b*Hq + hq.  Returns float64 [rows, D] (all rows:
     reshaped to [nb, Hq, D])."""
     q = np.ascontiguousarray(q)
@@ -209,18 +225,21 @@ def attend(planes: dict, q: np.ndarray, n: int, kbits: int, vbits: int,
     kt = np.ascontiguousarray(kt)
     vc = np.ascontiguousarray(planes["v_codes"], dtype=np.uint32)
     vm = np.ascontiguousarray(planes["v_meta"], dtype=np.uint32)
-    vt = None
-    if residual > 0:
-        vt = np.ascontiguousarray(np.ascontiguousarray(planes["v_tail"]).astype(q.dtype,
-                                                                              copy=False))
+    def opt(name, on):
+        if not on:
+            return None
+        return np.ascontiguousarray(np.ascontiguousarray(planes[name]).astype(q.dtype,
+                                                                            copy=False))
+    vt = opt("v_tail", residual > 0)
+    ks, vs = opt("k_sink", sink > 0), opt("v_sink", sink > 0)
     gcap = km.shape[2]
     tcap = vm.shape[2]
     r0, r1 = (0, nb * hq) if rows is None else rows
     out = np.zeros((r1 - r0, D), dtype=np.float64)
-    rc = lib().orc_attend(nb, hq, hkv, D, G, kbits, vbits, residual, gcap, tcap,
-                          float(base), _ptr(kc), _ptr(km), _ptr(kt), _ptr(vc), _ptr(vm),
-                          _ptr(vt) if vt is not None else None, _dtype_code(q), _ptr(q),
-                          n, r0, r1, _ptr(out))
+    P = lambda a: _ptr(a) if a is not None else None  # noqa: E731
+    rc = lib().orc_attend(nb, hq, hkv, D, G, kbits, vbits, residual, sink, gcap, tcap,
+                          float(base), _ptr(kc), _ptr(km), _ptr(kt), P(ks), _ptr(vc), _ptr(vm),
+                          P(vt), P(vs), _dtype_code(q), _ptr(q), n, r0, r1, _ptr(out))
     if rc != 0:
         raise ValueError("orc_attend failed")
     if rows is None:

@@ -37,6 +37,11 @@
  *      at least R (at most R + G - 1) recent tokens; a G-block is quantized
  *      when it leaves the window.  R = 0: Tq = G * floor(n / G) for keys and
  *      every value is quantized on arrival.
+ *      Sink window S (InnerQ keeps the first tokens in high precision;
+ *      [BITS], same section): keys and values of tokens [0, min(n, S)) stay
+ *      unquantized for good; the quantized region starts at S (a multiple of
+ *      G, so key groups stay aligned to token 0) and Tq is raised to at
+ *      least min(n, S).
  *   4. Keys are stored before the rotary position embedding; the rotation is
  *      applied after dequantization.  [BITS, "Rotary Embeddings Complicate
  *      the Keys"]; [GEOM, "What Data Scientists Should Do Next"].
@@ -59,6 +64,8 @@
  *   K_TAIL  dtype[nb][Hkv][R+G][D]      ring: token t >= Tq in slot t mod (R+G),
  *                                       verbatim (R = 0: slot t - Tq)
  *   V_TAIL  dtype[nb][Hkv][R+G][D]      the same for values (R > 0 only)
+ *   K_SINK  dtype[nb][Hkv][S][D]        token t < min(n, S) in slot t
+ *   V_SINK  dtype[nb][Hkv][S][D]        the same for values
  *
  * Input element types: ORC_F16 (IEEE binary16 bit patterns) or ORC_F32.
  */
@@ -210,21 +217,31 @@ int orc_quantized_tokens(int n, int G, int R)
     return a > 0 ? (a / G) * G : 0;
 }
 
+/* The same with a sink window S: tokens [0, min(n, S)) are sink tokens,
+ * [S, Tq) quantized, [Tq, n) in the tail ring. */
+int orc_quantized_end(int n, int G, int R, int S)
+{
+    int s = n < S ? n : S;
+    int q = orc_quantized_tokens(n, G, R);
+    return q > s ? q : s;
+}
+
 /* Key planes for T cached tokens with residual window R: groups g < Tq/G
  * are quantized per channel (group = one channel over tokens gG .. gG+G-1);
  * tokens t >= Tq are copied verbatim into ring slot t mod (R+G) of the tail.
  * Planes sized for gcap groups. */
 int orc_quantize_keys(const void* k, int dtype, int nb, int hkv, int T, int D,
-                      int G, int bits, int R, int gcap, uint32_t* k_codes,
-                      uint32_t* k_meta, void* k_tail)
+                      int G, int bits, int R, int S, int gcap, uint32_t* k_codes,
+                      uint32_t* k_meta, void* k_tail, void* k_sink)
 {
     if (G <= 0 || (G * bits) % 32 != 0 || T < 0 || R < 0 || R % G != 0 ||
-        T / G > gcap)
+        S < 0 || S % G != 0 || (S > 0 && !k_sink) || T / G > gcap)
         return -1;
     int wk = G * bits / 32;
-    int tq = orc_quantized_tokens(T, G, R);
+    int tq = orc_quantized_end(T, G, R, S);
     int ngroups = tq / G;
     int ring = R + G;
+    int ns = T < S ? T : S;
     size_t esz = (dtype == ORC_F16) ? 2 : 4;
     double* x = (double*)malloc(sizeof(double) * (size_t)G);
     uint8_t* codes = (uint8_t*)malloc((size_t)G);
@@ -236,7 +253,7 @@ int orc_quantize_keys(const void* k, int dtype, int nb, int hkv, int T, int D,
     for (int b = 0; b < nb; ++b)
         for (int h = 0; h < hkv; ++h) {
             size_t bh = (size_t)b * hkv + h;
-            for (int g = 0; g < ngroups; ++g)
+            for (int g = S / G; g < ngroups; ++g)
                 for (int c = 0; c < D; ++c) {
                     for (int j = 0; j < G; ++j)
                         x[j] = load_elem(k, dtype,
@@ -250,6 +267,9 @@ int orc_quantize_keys(const void* k, int dtype, int nb, int hkv, int T, int D,
             for (int t = tq; t < T; ++t)
                 memcpy((char*)k_tail + ((bh * ring + t % ring) * D) * esz,
                        (const char*)k + ((bh * T + t) * D) * esz, esz * D);
+            for (int t = 0; t < ns; ++t)
+                memcpy((char*)k_sink + ((bh * S + t) * D) * esz,
+                       (const char*)k + ((bh * T + t) * D) * esz, esz * D);
         }
     free(x);
     free(codes);
@@ -261,15 +281,18 @@ int orc_quantize_keys(const void* k, int dtype, int nb, int hkv, int T, int D,
  * tokens t < Tq are quantized and tokens t >= Tq copied verbatim into ring
  * slot t mod (R+G) of v_tail. */
 int orc_quantize_values(const void* v, int dtype, int nb, int hkv, int T,
-                        int D, int G, int bits, int R, int tcap,
-                        uint32_t* v_codes, uint32_t* v_meta, void* v_tail)
+                        int D, int G, int bits, int R, int S, int tcap,
+                        uint32_t* v_codes, uint32_t* v_meta, void* v_tail,
+                        void* v_sink)
 {
     if (G <= 0 || D % G != 0 || (G * bits) % 32 != 0 || T < 0 || T > tcap ||
-        R < 0 || R % G != 0 || (R > 0 && !v_tail))
+        R < 0 || R % G != 0 || (R > 0 && !v_tail) || S < 0 || S % G != 0 ||
+        (S > 0 && !v_sink))
         return -1;
     int wv = G * bits / 32;
     int ncg = D / G;
-    int tq = R > 0 ? orc_quantized_tokens(T, G, R) : T;
+    int tq = R > 0 ? orc_quantized_end(T, G, R, S) : T;
+    int ns = T < S ? T : S;
     int ring = R + G;
     size_t esz = (dtype == ORC_F16) ? 2 : 4;
     double* x = (double*)malloc(sizeof(double) * (size_t)G);
@@ -282,7 +305,7 @@ int orc_quantize_values(const void* v, int dtype, int nb, int hkv, int T,
     for (int b = 0; b < nb; ++b)
         for (int h = 0; h < hkv; ++h) {
             size_t bh = (size_t)b * hkv + h;
-            for (int t = 0; t < tq; ++t)
+            for (int t = ns; t < tq; ++t)
                 for (int cg = 0; cg < ncg; ++cg) {
                     for (int j = 0; j < G; ++j)
                         x[j] = load_elem(v, dtype,
@@ -295,6 +318,9 @@ int orc_quantize_values(const void* v, int dtype, int nb, int hkv, int T,
                 }
             for (int t = tq; t < T; ++t)
                 memcpy((char*)v_tail + ((bh * ring + t % ring) * D) * esz,
+                       (const char*)v + ((bh * T + t) * D) * esz, esz * D);
+            for (int t = 0; t < ns; ++t)
+                memcpy((char*)v_sink + ((bh * S + t) * D) * esz,
                        (const char*)v + ((bh * T + t) * D) * esz, esz * D);
         }
     free(x);
@@ -352,25 +378,29 @@ static void softmax_sum(const double* score, const double* vals, int n, int D,
 /* Decode attention over the quantized cache of n tokens (the planes above),
  * for the output rows r in [row_begin, row_end), r = b*Hq + hq.  Query head
  * hq reads KV head hq / (Hq/Hkv).  out holds (row_end-row_begin) x D doubles.
- *   keys t < Tq: dequantize per channel group, then rotate to position t;
+ *   keys and values t < min(n, S): sink slot t (keys rotated to position t);
+ *   keys S <= t < Tq: dequantize per channel group, rotate to position t;
  *   keys t >= Tq: tail ring slot t mod (R+G), rotated to position t;
- *   values t < Tq (all t when R = 0): dequantize; else v_tail ring slot;
+ *   values S <= t < Tq (all t >= S when R = 0): dequantize; else v_tail;
  *   query: rotated to position n-1;
  *   score_t = q'.k'_t / sqrt(D); out = sum_t softmax(score)_t * vhat_t. */
 int orc_attend(int nb, int hq, int hkv, int D, int G, int kbits, int vbits,
-               int R, int gcap, int tcap, double base, const uint32_t* k_codes,
-               const uint32_t* k_meta, const void* k_tail,
-               const uint32_t* v_codes, const uint32_t* v_meta,
-               const void* v_tail, int dtype, const void* q, int n,
-               int row_begin, int row_end, double* out)
+               int R, int S, int gcap, int tcap, double base,
+               const uint32_t* k_codes, const uint32_t* k_meta,
+               const void* k_tail, const void* k_sink, const uint32_t* v_codes,
+               const uint32_t* v_meta, const void* v_tail, const void* v_sink,
+               int dtype, const void* q, int n, int row_begin, int row_end,
+               double* out)
 {
     if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 || D % G != 0 ||
         n > tcap || n / G > gcap || row_begin < 0 || row_end > nb * hq ||
-        R < 0 || R % G != 0 || (R > 0 && !v_tail))
+        R < 0 || R % G != 0 || (R > 0 && !v_tail) || S < 0 || S % G != 0 ||
+        (S > 0 && (!k_sink || !v_sink)))
         return -1;
     int wk = G * kbits / 32, wv = G * vbits / 32, ncg = D / G;
-    int tq = orc_quantized_tokens(n, G, R);
+    int tq = orc_quantized_end(n, G, R, S);
     int vq = R > 0 ? tq : n;
+    int ns = n < S ? n : S;
     int ring = R + G;
     double* score = (double*)malloc(sizeof(double) * (size_t)n);
     double* vals = (double*)malloc(sizeof(double) * (size_t)n * D);
@@ -389,7 +419,10 @@ int orc_attend(int nb, int hq, int hkv, int D, int G, int kbits, int vbits,
             qr[c] = load_elem(q, dtype, (size_t)r * D + c);
         orc_rope(qr, D, (double)(n - 1), base);
         for (int t = 0; t < n; ++t) {
-            if (t < tq) {
+            if (t < ns) {
+                for (int c = 0; c < D; ++c)
+                    kr[c] = load_elem(k_sink, dtype, (bh * S + t) * D + c);
+            } else if (t < tq) {
                 int g = t / G, j = t % G;
                 for (int c = 0; c < D; ++c) {
                     size_t gc = (bh * gcap + g) * D + c;
@@ -406,7 +439,11 @@ int orc_attend(int nb, int hq, int hkv, int D, int G, int kbits, int vbits,
             for (int c = 0; c < D; ++c)
                 dot += qr[c] * kr[c];
             score[t] = dot / sqrt((double)D);
-            if (t < vq) {
+            if (t < ns) {
+                for (int c = 0; c < D; ++c)
+                    vals[(size_t)t * D + c] =
+                        load_elem(v_sink, dtype, (bh * S + t) * D + c);
+            } else if (t < vq) {
                 for (int cg = 0; cg < ncg; ++cg) {
                     size_t tc = (bh * tcap + t) * ncg + cg;
                     orc_unpack(v_codes + tc * wv, G, vbits, codes);
