@@ -71,26 +71,30 @@ def calibrate_copy():
     print(json.dumps({"calibration_copy_bytes": x.numel() * 4, "copies": 3}))
 
 
-def quantized_tokens(n: int, G: int, residual: int) -> int:
-    """Tokens [0, Tq) are quantized; with a residual window R the last
-    tokens (at least R) stay in full precision."""
+def quantized_tokens(n: int, G: int, residual: int, sink: int = 0) -> int:
+    """Tokens [min(n, sink), Tq) are quantized; with a residual window R the
+    last tokens (at least R) stay in full precision, with a sink the first
+    `sink` tokens."""
     a = n - residual
-    return a // G * G if a > 0 else 0
+    q = a // G * G if a > 0 else 0
+    return max(q, min(n, sink))
 
 
-def attend_bytes(cfg, n: int, residual: int = 0) -> int:
+def attend_bytes(cfg, n: int, residual: int = 0, sink: int = 0) -> int:
     """Algorithmic bytes of one decode-attention call at length n: packed key
     codes + key meta + unquantized keys + value codes + value meta (+
-    unquantized values with a residual window) + q + out."""
+    unquantized values of the windows) + q + out."""
     G, D = cfg.group, cfg.head_dim
     nbh = cfg.batch * cfg.kv_heads
     esz = 2 if cfg.dtype == "float16" else 4
-    tq = quantized_tokens(n, G, residual)
+    ns = min(n, sink)
+    tq = quantized_tokens(n, G, residual, sink)
     vq = tq if residual > 0 else n
-    return (nbh * tq * D * cfg.key_bits // 8 + nbh * (tq // G) * D * 4
-            + nbh * (n - tq) * D * esz
-            + nbh * vq * D * cfg.value_bits // 8 + nbh * vq * (D // G) * 4
-            + nbh * (n - vq) * D * esz
+    kq, vqn = tq - ns, vq - ns  # quantized key and value tokens
+    return (nbh * kq * D * cfg.key_bits // 8 + nbh * (kq // G) * D * 4
+            + nbh * (n - kq) * D * esz
+            + nbh * vqn * D * cfg.value_bits // 8 + nbh * vqn * (D // G) * 4
+            + nbh * (n - vqn) * D * esz
             + cfg.batch * cfg.q_heads * D * esz + cfg.batch * cfg.q_heads * D * 4)
 
 
@@ -103,18 +107,20 @@ def attend_flops(cfg, n: int) -> int:
     return cfg.batch * cfg.kv_heads * n * cfg.head_dim * (7 + 4 * qpk)
 
 
-def prefill_bytes(cfg, n: int, residual: int = 0) -> int:
+def prefill_bytes(cfg, n: int, residual: int = 0, sink: int = 0) -> int:
     """Quantize-and-pack of n tokens: K and V read once, planes written."""
     G, D = cfg.group, cfg.head_dim
     nbh = cfg.batch * cfg.kv_heads
     esz = 2 if cfg.dtype == "float16" else 4
-    tq = quantized_tokens(n, G, residual)
+    ns = min(n, sink)
+    tq = quantized_tokens(n, G, residual, sink)
     vq = tq if residual > 0 else n
+    kq, vqn = tq - ns, vq - ns
     return (2 * nbh * n * D * esz
-            + nbh * tq * D * cfg.key_bits // 8 + nbh * (tq // G) * D * 4
-            + nbh * (n - tq) * D * esz
-            + nbh * vq * D * cfg.value_bits // 8 + nbh * vq * (D // G) * 4
-            + nbh * (n - vq) * D * esz)
+            + nbh * kq * D * cfg.key_bits // 8 + nbh * (kq // G) * D * 4
+            + nbh * (n - kq) * D * esz
+            + nbh * vqn * D * cfg.value_bits // 8 + nbh * vqn * (D // G) * 4
+            + nbh * (n - vqn) * D * esz)
 
 
 class HipEvents:
@@ -155,7 +161,7 @@ class HipEvents:
         self.ev = []
 
 
-def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0):
+def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0, sink: int = 0):
     """The oracle (plain single-threaded fp64 C) on a bounded sample of the
     same workload: decode attention for whole sequences, rows timed until
     about budget_s seconds of CPU work."""
@@ -170,19 +176,22 @@ def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0):
     q = synth.make_query(cfg, 0, 0)
     rows_done, t_total, bytes_done = 0, 0.0, 0
     one = synth.scaled(cfg, batch=1)
-    per_row = attend_bytes(one, n, residual) / cfg.q_heads
+    per_row = attend_bytes(one, n, residual, sink) / cfg.q_heads
     for b in range(cfg.batch):
         k = synth.make_keys(cfg, 0, 0, n, seqs=[b])
         v = synth.make_values(cfg, 0, 0, n, seqs=[b])
-        kc, km, kt = oracle.quantize_keys(k, cfg.key_bits, cfg.group, residual=residual)
-        vals = oracle.quantize_values(v, cfg.value_bits, cfg.group, residual=residual)
-        pl = dict(k_codes=kc, k_meta=km, k_tail=kt, v_codes=vals[0], v_meta=vals[1])
+        kp = oracle.quantize_keys(k, cfg.key_bits, cfg.group, residual=residual, sink=sink)
+        vals = oracle.quantize_values(v, cfg.value_bits, cfg.group, residual=residual, sink=sink)
+        pl = dict(k_codes=kp[0], k_meta=kp[1], k_tail=kp[2], v_codes=vals[0], v_meta=vals[1])
         if residual > 0:
             pl["v_tail"] = vals[2]
+        if sink > 0:
+            pl["k_sink"], pl["v_sink"] = kp[3], vals[-1]
         for r in range(cfg.q_heads):
             t0 = time.perf_counter()
             oracle.attend(pl, q[b:b + 1], n, cfg.key_bits, cfg.value_bits, cfg.kv_heads,
-                          cfg.group, cfg.rope_base, rows=(r, r + 1), residual=residual)
+                          cfg.group, cfg.rope_base, rows=(r, r + 1), residual=residual,
+                          sink=sink)
             t_total += time.perf_counter() - t0
             rows_done += 1
             bytes_done += per_row
@@ -212,6 +221,8 @@ def main():
     ap.add_argument("--caches", type=int, default=0, help="rotating caches (0 = auto)")
     ap.add_argument("--residual", type=int, default=0,
                     help="recent tokens kept in full precision (a multiple of 32)")
+    ap.add_argument("--sink", type=int, default=0,
+                    help="first tokens kept in full precision (a multiple of 32)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
@@ -239,8 +250,8 @@ def main():
     tdt = torch.float16 if cfg.dtype == "float16" else torch.float32
     total_steps = args.warmup + args.steps
 
-    Rw = args.residual
-    cache_bytes = attend_bytes(cfg, n, Rw)
+    Rw, Sw = args.residual, args.sink
+    cache_bytes = attend_bytes(cfg, n, Rw, Sw)
     R = args.caches or max(2, math.ceil(2 * INFINITY_CACHE / cache_bytes) + 1)
     visits = math.ceil(total_steps / R)
     max_tokens = n + visits
@@ -257,7 +268,7 @@ def main():
 
     caches = [QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
                                cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev,
-                               residual=Rw)
+                               residual=Rw, sink=Sw)
               for _ in range(R)]
     # prefill (quantize-and-pack of the whole prompt), timed per cache after
     # one untimed prefill of a one-group cache (first launches load the code)
@@ -322,7 +333,7 @@ def main():
         raise RuntimeError("cache lengths do not match the steps issued")
 
     wall = t1 - t0
-    total_bytes = sum(attend_bytes(cfg, L, Rw) for L in lengths)
+    total_bytes = sum(attend_bytes(cfg, L, Rw, Sw) for L in lengths)
     value = total_bytes / wall / 1e9
     attend_ms = np.array([hev.elapsed_ms(2 * j, 2 * j + 1) for j in range(args.steps)])
     hev.close()
@@ -351,6 +362,7 @@ def main():
             "head_dim": cfg.head_dim, "context": n, "key_bits": cfg.key_bits,
             "value_bits": cfg.value_bits, "group": cfg.group, "kv_dtype": cfg.dtype,
             "residual": Rw,
+            "sink": Sw,
             "context_during_steps": [min(lengths), max(lengths)],
             "rotating_caches": R,
             "parallelism": "single GPU",
@@ -363,7 +375,7 @@ def main():
             "peak": FP32_VECTOR_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(cfg.name) if Rw == 0 else None,
+            "traffic": measured_traffic(cfg.name) if Rw == 0 and Sw == 0 else None,
             "kernel": "attend_kernel (decode attention); HIP events around each "
                       "kvq_attend_decode call in the timed loop",
             "flops_per_launch": int(flops_per_launch),
@@ -377,14 +389,15 @@ def main():
         "prefill": {
             "tokens": n - 1,
             "median_ms": round(float(np.median(pf_ms)), 4),
-            "GB_per_s": round(prefill_bytes(cfg, n - 1, Rw) / (np.median(pf_ms) / 1e3) / 1e9, 2),
+            "GB_per_s": round(prefill_bytes(cfg, n - 1, Rw, Sw) / (np.median(pf_ms) / 1e3) / 1e9,
+                              2),
             "tokens_per_s": round(cfg.batch * (n - 1) / (np.median(pf_ms) / 1e3), 1),
         },
     }
     for c in caches:
         c.close()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, n, residual=Rw)
+        res["cpu_baseline"] = cpu_baseline(cfg, n, residual=Rw, sink=Sw)
     print(json.dumps(res), flush=True)
 
 

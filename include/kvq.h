@@ -58,6 +58,9 @@
  *           ring: key token t >= Tq verbatim in slot t mod (R+G)
  *   V_TAIL  dtype[batch][kv_heads][R+G][head_dim]   (R > 0 only, else empty)
  *           ring: value token t >= Tq verbatim in slot t mod (R+G)
+ *   K_SINK  dtype[batch][kv_heads][S][head_dim]     (S = kvq_config.sink)
+ *   V_SINK  dtype[batch][kv_heads][S][head_dim]
+ *           key / value token t < min(n, S) verbatim in slot t
  * Residual window R = kvq_config.residual (the page "Your KV Cache Doesn't
  * Have a Bit Problem...", section "The Systems Tax, and Why It Is Not a
  * Detail": KIVI keeps the most recent tokens in full precision).  Tokens
@@ -66,6 +69,10 @@
  * R = 0 every value is quantized on arrival and only the < G keys of the
  * unfilled group wait).  With R > 0 at least R and at most R + G - 1 recent
  * tokens are unquantized; a G-block is quantized when it leaves the window.
+ * Sink window S = kvq_config.sink (same page and section: InnerQ keeps the
+ * first tokens in high precision): keys and values of tokens [0, min(n, S))
+ * stay unquantized for good, quantization starts at token S, and Tq above is
+ * raised to at least min(n, S).
  * The step and zero are each rounded once, to nearest-even, from the exact
  * value (range/(2^B-1) and the minimum); the code of x is the integer nearest
  * to (x - zero)/step computed exactly, ties to even, clamped to
@@ -113,10 +120,13 @@ typedef struct kvq_config {
     float rope_base;    /* > 1, e.g. 10000                                  */
     int32_t residual;   /* R: recent tokens kept in full precision, a
                            multiple of group in [0, 1024]; 0 = none         */
+    int32_t sink;       /* S: first tokens kept in full precision, a
+                           multiple of group in [0, 1024]; 0 = none         */
 } kvq_config;
 
 typedef struct kvq_layout {
     size_t k_codes, k_meta, v_codes, v_meta, k_tail, v_tail; /* byte offsets */
+    size_t k_sink, v_sink;
     size_t rope_group, rope_offset, partials;
     size_t total_bytes;   /* == kvq_workspace_bytes(cfg)                     */
     int32_t gcap, tcap;   /* Gcap and Tcap above                             */
@@ -142,11 +152,12 @@ int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes,
 
 /* Quantize a whole prompt of n_tokens tokens into the empty cache.
  * d_k, d_v: dtype[batch][kv_heads][n_tokens][head_dim], keys before the
- * rotary embedding.  With Tq as above for n = n_tokens: key groups
- * g < Tq/G are quantized per channel (K_CODES, K_META) and keys t >= Tq go to
- * the K_TAIL ring; R = 0: every value token is quantized per channel group
- * (V_CODES, V_META); R > 0: values t < Tq are quantized and values t >= Tq
- * go to the V_TAIL ring.  Sets n = n_tokens.
+ * rotary embedding.  With Tq as above for n = n_tokens: tokens
+ * t < min(n, S) go to the sinks; key groups S/G <= g < Tq/G are quantized
+ * per channel (K_CODES, K_META) and keys t >= Tq go to the K_TAIL ring;
+ * R = 0: every value token t >= S is quantized per channel group (V_CODES,
+ * V_META); R > 0: values S <= t < Tq are quantized and values t >= Tq go to
+ * the V_TAIL ring.  Sets n = n_tokens.
  * n_tokens == 0 is allowed and enqueues nothing.
  * Errors: KVQ_ERR_ARG (null handle or pointers with n_tokens > 0, negative
  * n_tokens), KVQ_ERR_STATE (n != 0), KVQ_ERR_CAPACITY (n_tokens >
@@ -155,13 +166,15 @@ int kvq_quantize_prefill(kvq_t* h, const void* d_k, const void* d_v,
                          int32_t n_tokens, void* stream);
 
 /* Append one token per sequence: d_k, d_v are dtype[batch][kv_heads]
- * [head_dim].  R = 0: the value is quantized at once; the key goes to tail
+ * [head_dim].  While n < S key and value go to sink slot n.  Otherwise,
+ * R = 0: the value is quantized at once; the key goes to tail
  * slot n mod G, and when that fills the tail (n+1 a multiple of G) the G
  * tail keys are quantized as key group n/G in the same launch.  R > 0: key
  * and value go to ring slot n mod (R+G); when n+1-R reaches a positive
  * multiple of G, the G-block b = (n+1-R)/G - 1 leaves the window and its
  * keys (group b) and values (tokens bG .. bG+G-1) are quantized from the
- * rings in the same launch.  Sets n = n + 1.
+ * rings in the same launch (a block inside the sink, bG < S, is not).  Sets
+ * n = n + 1.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_CAPACITY (n == max_tokens), KVQ_ERR_HIP. */
 int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v,
                      void* stream);

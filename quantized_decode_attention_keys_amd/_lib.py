@@ -47,6 +47,7 @@ class KvqConfig(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("rope_base", ctypes.c_float),
         ("residual", ctypes.c_int32),
+        ("sink", ctypes.c_int32),
     ]
 
 
@@ -58,6 +59,8 @@ class KvqLayout(ctypes.Structure):
         ("v_meta", ctypes.c_size_t),
         ("k_tail", ctypes.c_size_t),
         ("v_tail", ctypes.c_size_t),
+        ("k_sink", ctypes.c_size_t),
+        ("v_sink", ctypes.c_size_t),
         ("rope_group", ctypes.c_size_t),
         ("rope_offset", ctypes.c_size_t),
         ("partials", ctypes.c_size_t),

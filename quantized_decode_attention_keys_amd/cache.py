@@ -22,17 +22,19 @@ class QuantizedKVCache:
     [batch][kv_heads][head_dim] (append), q is [batch][q_heads][head_dim], all
     contiguous tensors of `dtype` on the cache's device; keys and queries are
     before the rotary embedding.  `residual` keeps the most recent tokens
-    (at least `residual`, fewer than `residual` + group) in full precision.
+    (at least `residual`, fewer than `residual` + group) in full precision,
+    `sink` the first `sink` tokens.
     Calls enqueue on the current torch stream (or `stream`) and return at
     once."""
 
     def __init__(self, batch, q_heads, kv_heads, head_dim, max_tokens, key_bits=2,
                  value_bits=2, dtype=torch.float16, rope_base=10000.0, group=32,
-                 device=None, residual=0):
+                 device=None, residual=0, sink=0):
         if dtype not in _DTYPES:
             raise TypeError("dtype must be torch.float16 or torch.float32")
         self.cfg = L.KvqConfig(batch, q_heads, kv_heads, head_dim, max_tokens, group,
-                               key_bits, value_bits, _DTYPES[dtype], rope_base, residual)
+                               key_bits, value_bits, _DTYPES[dtype], rope_base, residual,
+                               sink)
         self.dtype = dtype
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
             else torch.device(device)
@@ -114,6 +116,8 @@ class QuantizedKVCache:
             "k_tail": view(lay.k_tail, (nb, h, lay.tail_slots, D), self.dtype),
             "v_tail": view(lay.v_tail, (nb, h, lay.tail_slots if c.residual > 0 else 0, D),
                            self.dtype),
+            "k_sink": view(lay.k_sink, (nb, h, c.sink, D), self.dtype),
+            "v_sink": view(lay.v_sink, (nb, h, c.sink, D), self.dtype),
         }
 
     def close(self):

@@ -584,13 +584,17 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     const size_t bh = blockIdx.y / hgroups;
     const int b = (int)(bh / p.hkv), kvh = (int)(bh % p.hkv);
     const int head0 = (kvh * hgroups + (int)(blockIdx.y % hgroups)) * QPK;
-    // groups [0, ngq) are quantized; tokens [tq, n) are held verbatim in the
-    // tail rings (keys always, values with a residual window), in chunks of
-    // G tokens taken by the waves of the last split
-    const int tq = quantized_tokens(n, p.residual), ngq = tq / G;
-    const int nchunks = (n - tq + G - 1) / G;
-    const int g0 = (int)((long long)split * ngq / splits);
-    const int g1 = (int)((long long)(split + 1) * ngq / splits);
+    // Tokens [0, ns) are in the sinks, groups [gs, gs + ngq) quantized, and
+    // tokens [tq, n) in the tail rings (keys always, values with a residual
+    // window); sink and ring tokens go in chunks of G taken by the waves of
+    // the last split.
+    const int ns = n < p.sink ? n : p.sink;
+    const int tq = quantized_end(n, p.residual, p.sink), gs = p.sink / G;
+    const int ngq = tq / G > gs ? tq / G - gs : 0;
+    const int nsink_chunks = (ns + G - 1) / G;
+    const int nchunks = nsink_chunks + (n - tq + G - 1) / G;
+    const int g0 = gs + (int)((long long)split * ngq / splits);
+    const int g1 = gs + (int)((long long)(split + 1) * ngq / splits);
 
     // The first step's words go out before anything else: their HBM latency
     // overlaps the query rotation and the twiddle staging.
@@ -798,16 +802,20 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
 
     for (int ch = nwaves - 1 - wave; split == splits - 1 && ch < nchunks; ch += nwaves) {
         asm volatile("" : "+v"(tw_base));  // keep the twiddle reads in the loop
-        // One chunk of unquantized tokens t0 .. t0+cnt-1 (ring rows from
-        // row0, contiguous: the ring and t0 are multiples of G), scored like
-        // one more group after the quantized ones (the softmax is order-free):
-        // lane = channel pair, the tokens across its registers.
-        const int t0 = tq + ch * G, cnt = min(G, n - t0);
-        const size_t row0 = bh * (size_t)p.ring + t0 % p.ring;  // ring row of token t0
+        // One chunk of unquantized tokens t0 .. t0+cnt-1, from the sinks or
+        // the rings (rows from row0, contiguous: the ring and t0 are
+        // multiples of G), scored like one more group after the quantized
+        // ones (the softmax is order-free): lane = channel pair, the tokens
+        // across its registers.
+        const bool in_sink = ch < nsink_chunks;
+        const int t0 = in_sink ? ch * G : tq + (ch - nsink_chunks) * G;
+        const int cnt = min(G, (in_sink ? ns : n) - t0);
+        const size_t row0 = in_sink ? bh * (size_t)p.sink + t0 : bh * (size_t)p.ring + t0 % p.ring;
+        const void* const krows = in_sink ? p.k_sink : p.k_tail;
         float tx[G], ty[G];
         const size_t trow = row0 * D + 2 * i;  // element index of (token t0, channel 2i)
         if (p.dtype == 0) {
-            const uint32_t* t32 = reinterpret_cast<const uint32_t*>(p.k_tail) + trow / 2;
+            const uint32_t* t32 = reinterpret_cast<const uint32_t*>(krows) + trow / 2;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 const uint32_t w = (gsub == 0 && j < cnt) ? t32[(size_t)j * (D / 2)] : 0u;
@@ -815,7 +823,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 ty[j] = hi_h(w);
             }
         } else {
-            const float2* t64 = reinterpret_cast<const float2*>(p.k_tail) + trow / 2;
+            const float2* t64 = reinterpret_cast<const float2*>(krows) + trow / 2;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 const float2 w = (gsub == 0 && j < cnt) ? t64[(size_t)j * (D / 2)]
@@ -847,8 +855,8 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 acc = half_sum(acc);
             s[h] = acc;
         }
-        if (p.residual > 0) {
-            const char* vrows = static_cast<const char*>(p.v_tail) +
+        if (in_sink || p.residual > 0) {
+            const char* vrows = static_cast<const char*>(in_sink ? p.v_sink : p.v_tail) +
                                 row0 * D * (p.dtype == 0 ? 2 : 4);
             softmax_fp_values<D, KB, VB, QPK>(lane, t0, cnt, s, vrows, p.dtype, st);
         } else {

@@ -24,7 +24,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kTargetBlocks = 1024;  // attend blocks wanted per launch
 constexpr int kMaxSplits = 256;
-constexpr int kMaxResidual = 1024;  // tokens of the full-precision window
+constexpr int kMaxResidual = 1024;  // tokens of a full-precision window (residual, sink)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -35,14 +35,14 @@ int check_config(const kvq_config* c)
     if (c->batch < 1 || c->q_heads < 1 || c->kv_heads < 1 || c->head_dim < 1 ||
         c->max_tokens < 1 || c->group < 1 || c->key_bits < 1 || c->value_bits < 1 ||
         !(c->rope_base > 1.0f) || !std::isfinite(c->rope_base) || c->q_heads % c->kv_heads != 0 ||
-        (c->dtype != KVQ_F16 && c->dtype != KVQ_F32) || c->residual < 0)
+        (c->dtype != KVQ_F16 && c->dtype != KVQ_F32) || c->residual < 0 || c->sink < 0)
         return KVQ_ERR_ARG;
     const int qpk = c->q_heads / c->kv_heads;
     if (c->group != kvqi::kGroup || (c->head_dim != 64 && c->head_dim != 128) ||
         (c->key_bits != 2 && c->key_bits != 4 && c->key_bits != 8) ||
         (c->value_bits != 2 && c->value_bits != 4 && c->value_bits != 8) ||
         (qpk != 1 && qpk != 2 && qpk != 4 && qpk != 8) || c->residual % kvqi::kGroup != 0 ||
-        c->residual > kMaxResidual)
+        c->residual > kMaxResidual || c->sink % kvqi::kGroup != 0 || c->sink > kMaxResidual)
         return KVQ_ERR_UNSUPPORTED;
     // keep every plane index inside 2^31 elements per (sequence, head) and
     // the grid dimensions inside their limits
@@ -72,6 +72,8 @@ void make_layout(const kvq_config* c, kvq_layout* L)
     const size_t ring = (size_t)c->residual + G;
     L->k_tail = off;    off = align_up(off + nb * hkv * ring * D * esz);
     L->v_tail = off;    off = align_up(off + (c->residual > 0 ? nb * hkv * ring * D * esz : 0));
+    L->k_sink = off;    off = align_up(off + nb * hkv * (size_t)c->sink * D * esz);
+    L->v_sink = off;    off = align_up(off + nb * hkv * (size_t)c->sink * D * esz);
     L->rope_group = off; off = align_up(off + (size_t)gcap * (D / 2) * 8);
     L->rope_offset = off; off = align_up(off + G * (D / 2) * 8);
     L->partials = off;  off = align_up(off + nb * hq * (size_t)ms * (D + 2) * 4);
@@ -92,6 +94,8 @@ kvqi::Planes planes_of(const kvq* h)
     p.v_meta = reinterpret_cast<uint32_t*>(h->ws + L.v_meta);
     p.k_tail = h->ws + L.k_tail;
     p.v_tail = h->ws + L.v_tail;
+    p.k_sink = h->ws + L.k_sink;
+    p.v_sink = h->ws + L.v_sink;
     p.rope_group = reinterpret_cast<const float2*>(h->ws + L.rope_group);
     p.rope_offset = reinterpret_cast<const float2*>(h->ws + L.rope_offset);
     p.partials = reinterpret_cast<float*>(h->ws + L.partials);
@@ -107,6 +111,7 @@ kvqi::Planes planes_of(const kvq* h)
     p.dtype = h->cfg.dtype;
     p.residual = h->cfg.residual;
     p.ring = L.tail_slots;
+    p.sink = h->cfg.sink;
     return p;
 }
 
@@ -129,7 +134,10 @@ void attend_shape(const kvq* h, int n, int* splits_out, int* waves_out)
     const int qpk_all = h->cfg.q_heads / h->cfg.kv_heads;
     const int units = h->cfg.batch * h->cfg.kv_heads * (qpk_all / kvqi::block_heads(qpk_all));
     const int cus = h->cus > 0 ? h->cus : 256;
-    const int full_groups = kvqi::quantized_tokens(n, h->cfg.residual) / h->cfg.group;
+    // quantized groups: [sink/G, Tq/G), none while n < sink
+    const int qg = kvqi::quantized_end(n, h->cfg.residual, h->cfg.sink) / h->cfg.group -
+                   h->cfg.sink / h->cfg.group;
+    const int full_groups = qg > 0 ? qg : 0;
     const int groups_per_step = 64 / (h->cfg.head_dim / 2);
     const int wpc = kvqi::max_block_waves(kvqi::block_heads(qpk_all));
     const int cap = full_groups > 0 ? full_groups : 1;

@@ -26,11 +26,14 @@ struct Planes {
     uint32_t* v_meta;    // [nb][hkv][tcap][D/G]
     void* k_tail;        // dtype[nb][hkv][ring][D]: key t >= Tq in slot t mod ring
     void* v_tail;        // dtype[nb][hkv][ring][D]: the same for values (residual > 0)
+    void* k_sink;        // dtype[nb][hkv][sink][D]: key t < min(n, sink) in slot t
+    void* v_sink;        // dtype[nb][hkv][sink][D]: the same for values
     const float2* rope_group;   // [gcap][D/2]  (cos, sin) of g*G*theta_i
     const float2* rope_offset;  // [G][D/2]     (cos, sin) of j*theta_i
     float* partials;     // [nb*hq][max_splits][D+2]
     int nb, hq, hkv, D, kbits, vbits, gcap, tcap, max_splits, dtype;
     int residual, ring;  // R and R + G
+    int sink;            // S
 };
 
 // Tq: tokens [0, Tq) of an n-token cache are quantized (keys in whole
@@ -40,6 +43,15 @@ __host__ __device__ inline int quantized_tokens(int n, int residual)
 {
     const int a = n - residual;
     return a > 0 ? a / kGroup * kGroup : 0;
+}
+
+// With a sink window of S tokens: tokens [0, min(n, S)) stay in the sinks,
+// [S, Tq) are quantized, [Tq, n) are in the rings; Tq >= min(n, S).
+__host__ __device__ inline int quantized_end(int n, int residual, int sink)
+{
+    const int s = n < sink ? n : sink;
+    const int q = quantized_tokens(n, residual);
+    return q > s ? q : s;
 }
 
 // Launch wrappers (kvq_kernels.hip).  All enqueue on `stream` and return the

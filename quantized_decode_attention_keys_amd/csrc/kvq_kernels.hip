@@ -38,15 +38,15 @@ template <> __device__ __forceinline__ float to_f32<__half>(__half x) { return _
 // reduction; consecutive threads read consecutive channels of a token row.
 template <typename T, int BITS>
 __global__ __launch_bounds__(256) void quant_keys_kernel(Planes p, const T* __restrict__ k,
-                                                         int n_tokens, int ngroups)
+                                                         int n_tokens, int g_begin, int g_end)
 {
     constexpr int WK = G * BITS / 32;
     const int D = p.D;
     const int gpb = blockDim.x / D;
     const int c = threadIdx.x % D;
-    const int g = blockIdx.x * gpb + threadIdx.x / D;
+    const int g = g_begin + blockIdx.x * gpb + threadIdx.x / D;
     const size_t bh = blockIdx.y;
-    if (g >= ngroups)
+    if (g >= g_end)
         return;
     const T* src = k + (bh * (size_t)n_tokens + (size_t)g * G) * D + c;
     float x[G];
@@ -63,21 +63,22 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(Planes p, const T* __re
     p.k_meta[gc] = meta;
 }
 
-// Copy tokens [tq, n_tokens) of each sequence/head verbatim into a tail
-// ring (token t in slot t mod ring).
+// Copy tokens [t0, t1) of each sequence/head verbatim into a buffer of
+// `slots` token rows per sequence/head, token t in slot t mod slots (the
+// tail rings, or the sinks with slots = S > t).
 template <typename T>
-__global__ void copy_tail_kernel(Planes p, const T* __restrict__ src, T* __restrict__ ring,
-                                 int n_tokens, int tq, size_t total)
+__global__ void copy_tail_kernel(Planes p, const T* __restrict__ src, T* __restrict__ dst,
+                                 int slots, int n_tokens, int t0, int t1, size_t total)
 {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total)
         return;
     const int D = p.D;
-    const int rem = n_tokens - tq;
+    const int rem = t1 - t0;
     const int c = idx % D;
-    const int t = tq + (int)((idx / D) % rem);
+    const int t = t0 + (int)((idx / D) % rem);
     const size_t bh = idx / ((size_t)D * rem);
-    ring[(bh * p.ring + t % p.ring) * D + c] = src[(bh * n_tokens + t) * D + c];
+    dst[(bh * slots + t % slots) * D + c] = src[(bh * n_tokens + t) * D + c];
 }
 
 // One thread per (sequence*head, token, channel group): the group is G
@@ -133,6 +134,11 @@ __global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __rest
     const size_t bh = blockIdx.x;
     if (c >= D)
         return;  // D is a multiple of 64: whole waves only
+    if (n < p.sink) {  // the first tokens stay in the sinks
+        reinterpret_cast<T*>(p.k_sink)[(bh * p.sink + n) * D + c] = k[bh * D + c];
+        reinterpret_cast<T*>(p.v_sink)[(bh * p.sink + n) * D + c] = v[bh * D + c];
+        return;
+    }
     {
         const float x = to_f32(v[bh * D + c]);
         float mn = x, mx = x;
@@ -192,6 +198,11 @@ __global__ void append_residual_kernel(Planes p, const T* __restrict__ k,
     const size_t bh = blockIdx.x;
     if (c >= D)
         return;
+    if (n < p.sink) {  // the first tokens stay in the sinks
+        reinterpret_cast<T*>(p.k_sink)[(bh * p.sink + n) * D + c] = k[bh * D + c];
+        reinterpret_cast<T*>(p.v_sink)[(bh * p.sink + n) * D + c] = v[bh * D + c];
+        return;
+    }
     T* kring = reinterpret_cast<T*>(p.k_tail) + bh * p.ring * D;
     T* vring = reinterpret_cast<T*>(p.v_tail) + bh * p.ring * D;
     const int slot = n % p.ring;
@@ -201,6 +212,8 @@ __global__ void append_residual_kernel(Planes p, const T* __restrict__ k,
     if (aged < G || aged % G != 0)
         return;
     const int b = aged / G - 1;
+    if (b * G < p.sink)
+        return;  // that block is in the sinks
     {
         float x[G];
 #pragma unroll
@@ -238,36 +251,43 @@ template <typename T>
 hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tokens,
                               hipStream_t stream)
 {
-    const int tq = quantized_tokens(n_tokens, p.residual);
-    const int ngroups = tq / G;
+    // sink [0, ns), quantized [S, tq), rings [tq, n_tokens)
+    const int ns = n_tokens < p.sink ? n_tokens : p.sink;
+    const int tq = quantized_end(n_tokens, p.residual, p.sink);
+    const int g_begin = p.sink / G, g_end = tq / G;
     const int nbh = p.nb * p.hkv;
-    if (ngroups > 0) {
+    if (g_end > g_begin) {
         const int gpb = 256 / p.D;
-        dim3 grid((ngroups + gpb - 1) / gpb, nbh);
+        dim3 grid((g_end - g_begin + gpb - 1) / gpb, nbh);
         switch (p.kbits) {
-        case 2: quant_keys_kernel<T, 2><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, ngroups); break;
-        case 4: quant_keys_kernel<T, 4><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, ngroups); break;
-        case 8: quant_keys_kernel<T, 8><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, ngroups); break;
+        case 2: quant_keys_kernel<T, 2><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
+        case 4: quant_keys_kernel<T, 4><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
+        case 8: quant_keys_kernel<T, 8><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
         }
     }
-    const size_t rest = (size_t)nbh * (n_tokens - tq) * p.D;
-    const unsigned rblocks = (unsigned)((rest + 255) / 256);
-    if (rest > 0)
-        copy_tail_kernel<T><<<rblocks, 256, 0, stream>>>(p, k, static_cast<T*>(p.k_tail), n_tokens,
-                                                         tq, rest);
-    // values: all quantized without a window; with one, [0, tq) quantized
-    // and the rest copied to the value ring
+    auto copy = [&](const T* src, void* dst, int slots, int t0, int t1) {
+        const size_t total = (size_t)nbh * (t1 - t0) * p.D;
+        if (total > 0)
+            copy_tail_kernel<T><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
+                p, src, static_cast<T*>(dst), slots, n_tokens, t0, t1, total);
+    };
+    copy(k, p.k_tail, p.ring, tq, n_tokens);
+    copy(k, p.k_sink, p.sink, 0, ns);
+    copy(v, p.v_sink, p.sink, 0, ns);
+    // values: every token from S on quantized without a window; with one,
+    // [S, tq) quantized and the rest copied to the value ring
     const int vq = p.residual > 0 ? tq : n_tokens;
-    if (p.residual > 0 && rest > 0)
-        copy_tail_kernel<T><<<rblocks, 256, 0, stream>>>(p, v, static_cast<T*>(p.v_tail), n_tokens,
-                                                         tq, rest);
-    const size_t vg = (size_t)nbh * vq * (p.D / G);
+    if (p.residual > 0)
+        copy(v, p.v_tail, p.ring, tq, n_tokens);
+    const int v0 = ns;  // first quantized value token (S, or n_tokens while n_tokens < S)
+    const size_t vg = vq > v0 ? (size_t)nbh * (vq - v0) * (p.D / G) : 0;
     const unsigned vblocks = (unsigned)((vg + 255) / 256);
+    const T* vsrc = v + (size_t)v0 * p.D;  // token v0 of sequence/head 0; rows of n_tokens
     if (vg > 0) {
         switch (p.vbits) {
-        case 2: quant_values_kernel<T, 2><<<vblocks, 256, 0, stream>>>(p, v, vq, n_tokens, 0, vg); break;
-        case 4: quant_values_kernel<T, 4><<<vblocks, 256, 0, stream>>>(p, v, vq, n_tokens, 0, vg); break;
-        case 8: quant_values_kernel<T, 8><<<vblocks, 256, 0, stream>>>(p, v, vq, n_tokens, 0, vg); break;
+        case 2: quant_values_kernel<T, 2><<<vblocks, 256, 0, stream>>>(p, vsrc, vq - v0, n_tokens, v0, vg); break;
+        case 4: quant_values_kernel<T, 4><<<vblocks, 256, 0, stream>>>(p, vsrc, vq - v0, n_tokens, v0, vg); break;
+        case 8: quant_values_kernel<T, 8><<<vblocks, 256, 0, stream>>>(p, vsrc, vq - v0, n_tokens, v0, vg); break;
         }
     }
     return hipGetLastError();

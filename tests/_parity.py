@@ -20,10 +20,10 @@ def to_gpu(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
 
 
-def make_cache(cfg, max_tokens, residual=0):
+def make_cache(cfg, max_tokens, residual=0, sink=0):
     return QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
                             cfg.key_bits, cfg.value_bits, _TORCH[cfg.np_dtype],
-                            rope_base=cfg.rope_base, device=dev(), residual=residual)
+                            rope_base=cfg.rope_base, device=dev(), residual=residual, sink=sink)
 
 
 def gpu_planes(cache):
@@ -35,30 +35,33 @@ def gpu_planes(cache):
     return out
 
 
-def oracle_planes(cfg, k, v, max_tokens, residual=0):
-    kc, km, kt = oracle.quantize_keys(k, cfg.key_bits, cfg.group, max_tokens=max_tokens,
-                                      residual=residual)
+def oracle_planes(cfg, k, v, max_tokens, residual=0, sink=0):
+    kp = oracle.quantize_keys(k, cfg.key_bits, cfg.group, max_tokens=max_tokens,
+                              residual=residual, sink=sink)
     vals = oracle.quantize_values(v, cfg.value_bits, cfg.group, max_tokens=max_tokens,
-                                  residual=residual)
-    pl = dict(k_codes=kc, k_meta=km, k_tail=kt, v_codes=vals[0], v_meta=vals[1])
+                                  residual=residual, sink=sink)
+    pl = dict(k_codes=kp[0], k_meta=kp[1], k_tail=kp[2], v_codes=vals[0], v_meta=vals[1])
     if residual > 0:
         pl["v_tail"] = vals[2]
+    if sink > 0:
+        pl["k_sink"], pl["v_sink"] = kp[3], vals[-1]
     return pl
 
 
-def assert_planes_equal(gp, op, n, G=32, seqs=None, residual=0):
+def assert_planes_equal(gp, op, n, G=32, seqs=None, residual=0, sink=0):
     """Bit-exact comparison of every slot that holds data at length n: codes
-    and metadata of the quantized tokens, ring slots of the others."""
-    tq = oracle.quantized_tokens(n, G, residual)
+    and metadata of the quantized tokens, ring and sink slots of the others."""
+    tq = oracle.quantized_tokens(n, G, residual, sink)
     vq = tq if residual > 0 else n
+    ns = min(n, sink)
     ring = residual + G
     # seqs selects GPU sequences; op holds the oracle planes of just those
     sel = slice(None) if seqs is None else list(seqs)
     g = {k: a[sel] for k, a in gp.items()}
     o = op
-    for name, lim in (("k_codes", tq // G), ("k_meta", tq // G), ("v_codes", vq),
-                      ("v_meta", vq)):
-        a, b = g[name][:, :, :lim], o[name][:, :, :lim]
+    for name, lo, hi in (("k_codes", sink // G, tq // G), ("k_meta", sink // G, tq // G),
+                         ("v_codes", ns, vq), ("v_meta", ns, vq)):
+        a, b = g[name][:, :, lo:hi], o[name][:, :, lo:hi]
         if not np.array_equal(a, b):
             bad = np.argwhere(a != b)
             raise AssertionError(f"{name}: {len(bad)} mismatches, first at {bad[0].tolist()}: "
@@ -67,6 +70,9 @@ def assert_planes_equal(gp, op, n, G=32, seqs=None, residual=0):
     tails = ("k_tail", "v_tail") if residual > 0 else ("k_tail",)
     for name in tails:
         at, bt = g[name][:, :, slots], o[name][:, :, slots]
+        assert np.array_equal(at.view(np.uint8), bt.view(np.uint8)), f"{name} differs"
+    for name in (("k_sink", "v_sink") if sink > 0 else ()):
+        at, bt = g[name][:, :, :ns], o[name][:, :, :ns]
         assert np.array_equal(at.view(np.uint8), bt.view(np.uint8)), f"{name} differs"
 
 

@@ -49,7 +49,8 @@ def test_layout_sizes_alignment_and_order():
     assert st == L.KVQ_OK
     assert lay.gcap == 32 and lay.tcap == 1024
     offs = [lay.k_codes, lay.k_meta, lay.v_codes, lay.v_meta, lay.k_tail, lay.v_tail,
-            lay.rope_group, lay.rope_offset, lay.partials, lay.total_bytes]
+            lay.k_sink, lay.v_sink, lay.rope_group, lay.rope_offset, lay.partials,
+            lay.total_bytes]
     assert offs == sorted(offs)
     assert all(o % 256 == 0 for o in offs)
     nb, h, D = 2, 2, 128
@@ -58,10 +59,18 @@ def test_layout_sizes_alignment_and_order():
     assert lay.v_meta - lay.v_codes >= nb * h * 1024 * 4 * 4 * 4     # D/G = 4, Wv = 4
     assert lay.k_tail - lay.v_meta >= nb * h * 1024 * 4 * 4
     assert lay.v_tail - lay.k_tail >= nb * h * 32 * D * 2
-    assert lay.rope_group == lay.v_tail  # no value ring without a residual window
+    assert lay.k_sink == lay.v_tail == lay.v_sink == lay.rope_group  # no window planes
     assert lay.tail_slots == 32
     assert L.kvq_workspace_bytes(c) == lay.total_bytes
     assert lay.max_splits >= 1
+
+
+def test_layout_with_sink_window():
+    st, lay = L.kvq_layout_for(cfg(sink=64))
+    assert st == L.KVQ_OK
+    nb, h, D = 2, 2, 128
+    assert lay.v_sink - lay.k_sink >= nb * h * 64 * D * 2
+    assert lay.rope_group - lay.v_sink >= nb * h * 64 * D * 2
 
 
 def test_layout_with_residual_window():
@@ -70,7 +79,7 @@ def test_layout_with_residual_window():
     assert st == L.KVQ_OK and lay.tail_slots == 160
     nb, h, D = 2, 2, 128
     assert lay.v_tail - lay.k_tail >= nb * h * 160 * D * 2
-    assert lay.rope_group - lay.v_tail >= nb * h * 160 * D * 2
+    assert lay.k_sink - lay.v_tail >= nb * h * 160 * D * 2
     _, lay0 = L.kvq_layout_for(cfg())
     assert lay.total_bytes > lay0.total_bytes
 
@@ -89,6 +98,9 @@ def test_layout_with_residual_window():
     ("residual", -32, L.KVQ_ERR_ARG),
     ("residual", 48, L.KVQ_ERR_UNSUPPORTED),      # not a multiple of the group
     ("residual", 1056, L.KVQ_ERR_UNSUPPORTED),    # beyond the 1024-token window
+    ("sink", -32, L.KVQ_ERR_ARG),
+    ("sink", 40, L.KVQ_ERR_UNSUPPORTED),
+    ("sink", 2048, L.KVQ_ERR_UNSUPPORTED),
 ])
 def test_bad_configs_rejected_on_host(field, value, status):
     c = cfg(**{field: value})
