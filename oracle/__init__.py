@@ -74,6 +74,12 @@ def lib() -> ctypes.CDLL:
         L.orc_attend.restype = i
         L.orc_attend_dense.argtypes = [i, i, i, i, d, P, P, i, P, i, i, i, P]
         L.orc_attend_dense.restype = i
+        L.orc_attend_geometry.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, d, P, P, P,
+                                          P, P, P, P, P, i, P, i, i, i, P]
+        L.orc_attend_geometry.restype = i
+        L.orc_error_metrics.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, d, P, P, P,
+                                        P, P, P, P, P, i, P, P, P, i, i, i, P]
+        L.orc_error_metrics.restype = i
         _lib = L
     return _lib
 
@@ -264,3 +270,119 @@ def attend_dense(k: np.ndarray, v: np.ndarray, q: np.ndarray,
     if rows is None:
         return out.reshape(nb, hq, D)
     return out
+
+
+# -------------------------------------------------------- geometry ablation
+
+KEYS_PER_TOKEN = 1
+VALUES_PER_CHANNEL = 2
+GEOMETRIES = {"kivi": 0, "keys_per_token": KEYS_PER_TOKEN,
+              "values_per_channel": VALUES_PER_CHANNEL,
+              "both_flipped": KEYS_PER_TOKEN | VALUES_PER_CHANNEL}
+
+
+def geometry_planes(k: np.ndarray, v: np.ndarray, kbits: int, vbits: int, geometry: int,
+                    G: int = 32, max_tokens=None) -> dict:
+    """Planes of a cache in any geometry (no windows).  A flipped operand
+    takes the other operand's layout: keys per token are grouped like values
+    (``k_codes`` [nb][Hkv][Tcap][D/G][Wk], ``k_meta`` [nb][Hkv][Tcap][D/G], no
+    key tail); values per channel are grouped like keys (``v_codes``
+    [nb][Hkv][Gcap][D][Wv], ``v_meta`` [nb][Hkv][Gcap][D], ``v_tail`` of G
+    slots for the unfilled group)."""
+    pl = {}
+    if geometry & KEYS_PER_TOKEN:
+        pl["k_codes"], pl["k_meta"] = quantize_values(k, kbits, G, max_tokens)
+        nb, hkv, _, D = k.shape
+        pl["k_tail"] = np.zeros((nb, hkv, G, D), dtype=k.dtype)
+    else:
+        pl["k_codes"], pl["k_meta"], pl["k_tail"] = quantize_keys(k, kbits, G, max_tokens)
+    if geometry & VALUES_PER_CHANNEL:
+        pl["v_codes"], pl["v_meta"], pl["v_tail"] = quantize_keys(v, vbits, G, max_tokens)
+    else:
+        pl["v_codes"], pl["v_meta"] = quantize_values(v, vbits, G, max_tokens)
+    return pl
+
+
+def _plane_args(planes, dtype, residual, sink, geometry):
+    def u32(name):
+        return np.ascontiguousarray(planes[name], dtype=np.uint32)
+
+    def opt(name, on):
+        if not on:
+            return None
+        return np.ascontiguousarray(np.ascontiguousarray(planes[name]).astype(dtype,
+                                                                            copy=False))
+    kc, km, vc, vm = u32("k_codes"), u32("k_meta"), u32("v_codes"), u32("v_meta")
+    kt = opt("k_tail", True)
+    vt = opt("v_tail", residual > 0 or bool(geometry & VALUES_PER_CHANNEL))
+    ks, vs = opt("k_sink", sink > 0), opt("v_sink", sink > 0)
+    # capacities from whichever plane is grouped per channel / per token
+    if geometry & KEYS_PER_TOKEN:
+        tcap = km.shape[2]
+        gcap = vm.shape[2] if geometry & VALUES_PER_CHANNEL else tcap // 32
+    else:
+        gcap = km.shape[2]
+        tcap = gcap * 32 if geometry & VALUES_PER_CHANNEL else vm.shape[2]
+    return (kc, km, kt, ks, vc, vm, vt, vs), gcap, tcap
+
+
+def attend_geometry(planes: dict, q: np.ndarray, n: int, kbits: int, vbits: int, hkv: int,
+                    geometry: int, G: int = 32, base: float = 10000.0, rows=None,
+                    residual: int = 0, sink: int = 0) -> np.ndarray:
+    """Decode attention over a cache in any geometry (``geometry_planes``);
+    geometry 0 also takes the residual and sink windows of ``attend``."""
+    q = np.ascontiguousarray(q)
+    nb, hq, D = q.shape
+    arrs, gcap, tcap = _plane_args(planes, q.dtype, residual, sink, geometry)
+    r0, r1 = (0, nb * hq) if rows is None else rows
+    out = np.zeros((r1 - r0, D), dtype=np.float64)
+    P = lambda a: _ptr(a) if a is not None else None  # noqa: E731
+    rc = lib().orc_attend_geometry(nb, hq, hkv, D, G, kbits, vbits, geometry, residual, sink,
+                                   gcap, tcap, float(base), *[P(a) for a in arrs],
+                                   _dtype_code(q), _ptr(q), n, r0, r1, _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_attend_geometry failed")
+    return out.reshape(nb, hq, D) if rows is None else out
+
+
+METRICS = ("key_error", "score_error", "value_error", "value_output_rel_error",
+           "output_rel_error")
+
+
+def summarize_metrics(rows: np.ndarray) -> dict:
+    """Row sums (see ``error_metrics``) -> the five metrics, each a mean over
+    output rows: key and value reconstruction error (Frobenius norm over the
+    row's KV head), attention-score error (L2 norm of the weight
+    difference), relative output error of the value side and end to end."""
+    rows = np.asarray(rows, dtype=np.float64)
+    return {
+        "key_error": float(np.mean(np.sqrt(rows[:, 4]))),
+        "score_error": float(np.mean(np.sqrt(rows[:, 0]))),
+        "value_error": float(np.mean(np.sqrt(rows[:, 5]))),
+        "value_output_rel_error": float(np.mean(np.sqrt(rows[:, 1] / rows[:, 2]))),
+        "output_rel_error": float(np.mean(np.sqrt(rows[:, 3] / rows[:, 2]))),
+    }
+
+
+def error_metrics(planes: dict, k: np.ndarray, v: np.ndarray, q: np.ndarray, n: int,
+                  kbits: int, vbits: int, hkv: int, geometry: int = 0, G: int = 32,
+                  base: float = 10000.0, rows=None, residual: int = 0, sink: int = 0):
+    """Error where it is consumed for the cache holding the unquantized
+    k, v [nb][Hkv][n][D] (q's dtype).  Returns (summary dict, per-row sums
+    [rows][6]): sum (ahat - a)^2, |A vhat - A v|^2, |A v|^2,
+    |Ahat vhat - A v|^2, sum (khat - k)^2 and sum (vhat - v)^2."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k, dtype=q.dtype)
+    v = np.ascontiguousarray(v, dtype=q.dtype)
+    nb, hq, D = q.shape
+    arrs, gcap, tcap = _plane_args(planes, q.dtype, residual, sink, geometry)
+    r0, r1 = (0, nb * hq) if rows is None else rows
+    out = np.zeros((r1 - r0, 6), dtype=np.float64)
+    P = lambda a: _ptr(a) if a is not None else None  # noqa: E731
+    rc = lib().orc_error_metrics(nb, hq, hkv, D, G, kbits, vbits, geometry, residual, sink,
+                                 gcap, tcap, float(base), *[P(a) for a in arrs],
+                                 _dtype_code(q), _ptr(k), _ptr(v), _ptr(q), n, r0, r1,
+                                 _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_error_metrics failed")
+    return summarize_metrics(out), out

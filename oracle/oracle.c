@@ -51,6 +51,20 @@
  *   5. Attention output = softmax-weighted sum of the value vectors over all
  *      cached tokens, scores scaled by 1/sqrt(D).  [BITS, "Values: Where the
  *      Intuition Breaks"].  Softmax is the plain two-pass form.
+ *   6. Geometry ablation ([BITS], lede and "Keys: The Outliers Live in Fixed
+ *      Channels", "Values: Where the Intuition Breaks"): the same 2 bits
+ *      spent along the other axis -- keys per token (a group is G channels
+ *      of one token, quantized on arrival) and/or values per channel (a group
+ *      is one channel over G tokens; unfilled value groups wait in a tail
+ *      like the keys').  The planes of a flipped operand take the other
+ *      operand's layout.  Error where it is consumed, against the unquantized
+ *      inputs (reading: per output row, i.e. per (sequence, query head), then
+ *      averaged over rows): key and value reconstruction error (Frobenius
+ *      norm over the row's KV head), attention-score error (L2 norm of the
+ *      difference of the softmax weights from stored and from unquantized
+ *      keys), the value side's relative output error (weights from
+ *      unquantized keys, stored against unquantized values) and the
+ *      end-to-end relative output error.
  *
  * Packed layout (the bit-exact contract shared with the GPU library, which
  * implements it separately):
@@ -502,5 +516,218 @@ int orc_attend_dense(int nb, int hq, int hkv, int D, double base,
         softmax_sum(score, vals, n, D, out + (size_t)(r - row_begin) * D);
     }
     free(score); free(vals); free(qr); free(kr);
+    return 0;
+}
+
+/* ------------------------------------------------------ geometry ablation */
+
+#define ORC_KEYS_PER_TOKEN 1
+#define ORC_VALUES_PER_CHANNEL 2
+
+/* Row t (D elements, as stored: dequantized or verbatim) of one operand of
+ * sequence/head bh in an n-token cache.
+ *   per_token: groups are G channels of one token, planes
+ *              codes[bh][tcap][D/G][W], meta[bh][tcap][D/G]; every token
+ *              t >= ns is quantized unless a residual window R > 0 keeps
+ *              [tq, n) in the ring (ring_values).
+ *   otherwise: groups are one channel over G tokens, planes
+ *              codes[bh][gcap][D][W], meta[bh][gcap][D]; tokens [ns, tq) are
+ *              quantized and [tq, n) sit in ring slot t mod ring.
+ *   t < ns:    sink row t. */
+static void stored_row(int per_token, int ring_values, const uint32_t* codes,
+                       const uint32_t* meta, const void* ring_buf,
+                       const void* sink_buf, int dtype, size_t bh, int t, int n,
+                       int D, int G, int bits, int R, int S, int gcap, int tcap,
+                       double* row)
+{
+    int w = G * bits / 32, ncg = D / G, ring = R + G;
+    int ns = n < S ? n : S;
+    int tq = orc_quantized_end(n, G, R, S);
+    if (t < ns) {
+        for (int c = 0; c < D; ++c)
+            row[c] = load_elem(sink_buf, dtype, (bh * S + t) * D + c);
+    } else if (per_token && (!ring_values || t < tq)) {
+        for (int cg = 0; cg < ncg; ++cg) {
+            size_t tc = (bh * tcap + t) * ncg + cg;
+            for (int j = 0; j < G; ++j)
+                row[cg * G + j] = dequant(meta[tc],
+                                          orc_code_at(codes + tc * w, j, bits));
+        }
+    } else if (!per_token && t < tq) {
+        int g = t / G, j = t % G;
+        for (int c = 0; c < D; ++c) {
+            size_t gc = (bh * gcap + g) * D + c;
+            row[c] = dequant(meta[gc], orc_code_at(codes + gc * w, j, bits));
+        }
+    } else {
+        for (int c = 0; c < D; ++c)
+            row[c] = load_elem(ring_buf, dtype, (bh * ring + t % ring) * D + c);
+    }
+}
+
+/* Decode attention over a cache in any geometry (the bits of geom above),
+ * rows [row_begin, row_end) as in orc_attend.  Keys per channel with R > 0
+ * or S > 0 read the sink and ring as orc_attend does; the flipped
+ * geometries are defined without windows (R = S = 0). */
+int orc_attend_geometry(int nb, int hq, int hkv, int D, int G, int kbits,
+                        int vbits, int geom, int R, int S, int gcap, int tcap,
+                        double base, const uint32_t* k_codes,
+                        const uint32_t* k_meta, const void* k_tail,
+                        const void* k_sink, const uint32_t* v_codes,
+                        const uint32_t* v_meta, const void* v_tail,
+                        const void* v_sink, int dtype, const void* q, int n,
+                        int row_begin, int row_end, double* out)
+{
+    if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 || D % G != 0 ||
+        n > tcap || n / G > gcap || row_begin < 0 || row_end > nb * hq ||
+        geom < 0 || geom > 3 || R < 0 || R % G != 0 || S < 0 || S % G != 0 ||
+        (geom != 0 && (R != 0 || S != 0)) || (S > 0 && (!k_sink || !v_sink)) ||
+        ((R > 0 || (geom & ORC_VALUES_PER_CHANNEL)) && !v_tail))
+        return -1;
+    int kpt = (geom & ORC_KEYS_PER_TOKEN) != 0;
+    int vpt = (geom & ORC_VALUES_PER_CHANNEL) == 0;
+    double* score = (double*)malloc(sizeof(double) * (size_t)n);
+    double* vals = (double*)malloc(sizeof(double) * (size_t)n * D);
+    double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!score || !vals || !qr || !kr) {
+        free(score); free(vals); free(qr); free(kr);
+        return -2;
+    }
+    int group = hq / hkv;
+    for (int r = row_begin; r < row_end; ++r) {
+        int b = r / hq, h = r % hq, kvh = h / group;
+        size_t bh = (size_t)b * hkv + kvh;
+        for (int c = 0; c < D; ++c)
+            qr[c] = load_elem(q, dtype, (size_t)r * D + c);
+        orc_rope(qr, D, (double)(n - 1), base);
+        for (int t = 0; t < n; ++t) {
+            stored_row(kpt, 0, k_codes, k_meta, k_tail, k_sink, dtype, bh, t, n,
+                       D, G, kbits, R, S, gcap, tcap, kr);
+            orc_rope(kr, D, (double)t, base);
+            double dot = 0.0;
+            for (int c = 0; c < D; ++c)
+                dot += qr[c] * kr[c];
+            score[t] = dot / sqrt((double)D);
+            stored_row(vpt, R > 0, v_codes, v_meta, v_tail, v_sink, dtype, bh, t,
+                       n, D, G, vbits, R, S, gcap, tcap, vals + (size_t)t * D);
+        }
+        softmax_sum(score, vals, n, D, out + (size_t)(r - row_begin) * D);
+    }
+    free(score); free(vals); free(qr); free(kr);
+    return 0;
+}
+
+/* Softmax weights (two-pass) of n scores, in place. */
+static void softmax_weights(double* s, int n)
+{
+    double m = s[0], l = 0.0;
+    for (int t = 1; t < n; ++t)
+        if (s[t] > m) m = s[t];
+    for (int t = 0; t < n; ++t) {
+        s[t] = exp(s[t] - m);
+        l += s[t];
+    }
+    for (int t = 0; t < n; ++t)
+        s[t] /= l;
+}
+
+/* Error where it is consumed, per output row r in [row_begin, row_end)
+ * (6 doubles each in rows_out), for a cache of n tokens holding the
+ * unquantized keys k and values v ([nb][Hkv][n][D], the cache's dtype):
+ *   [0] sum_t (ahat_t - a_t)^2      a = softmax(q'.RoPE(k_t)/sqrt(D)),
+ *                                   ahat the same from the stored keys
+ *   [1] |sum_t a_t vhat_t - sum_t a_t v_t|^2     (stored values, exact weights)
+ *   [2] |sum_t a_t v_t|^2                        (the reference output)
+ *   [3] |sum_t ahat_t vhat_t - sum_t a_t v_t|^2  (end to end)
+ *   [4] sum_{t,c} (khat - k)^2 over the row's KV head (before the rotation)
+ *   [5] sum_{t,c} (vhat - v)^2 over the row's KV head
+ * "Stored" is what the cache holds: dequantized codes, or the verbatim tail,
+ * ring and sink rows. */
+int orc_error_metrics(int nb, int hq, int hkv, int D, int G, int kbits,
+                      int vbits, int geom, int R, int S, int gcap, int tcap,
+                      double base, const uint32_t* k_codes,
+                      const uint32_t* k_meta, const void* k_tail,
+                      const void* k_sink, const uint32_t* v_codes,
+                      const uint32_t* v_meta, const void* v_tail,
+                      const void* v_sink, int dtype, const void* k,
+                      const void* v, const void* q, int n, int row_begin,
+                      int row_end, double* rows_out)
+{
+    if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 || D % G != 0 ||
+        n > tcap || n / G > gcap || row_begin < 0 || row_end > nb * hq ||
+        geom < 0 || geom > 3 || R < 0 || R % G != 0 || S < 0 || S % G != 0 ||
+        (geom != 0 && (R != 0 || S != 0)) || (S > 0 && (!k_sink || !v_sink)) ||
+        ((R > 0 || (geom & ORC_VALUES_PER_CHANNEL)) && !v_tail))
+        return -1;
+    int kpt = (geom & ORC_KEYS_PER_TOKEN) != 0;
+    int vpt = (geom & ORC_VALUES_PER_CHANNEL) == 0;
+    size_t nd = (size_t)n * D;
+    double* a = (double*)malloc(sizeof(double) * (size_t)n);
+    double* ah = (double*)malloc(sizeof(double) * (size_t)n);
+    double* kx = (double*)malloc(sizeof(double) * nd);
+    double* kh = (double*)malloc(sizeof(double) * nd);
+    double* vx = (double*)malloc(sizeof(double) * nd);
+    double* vh = (double*)malloc(sizeof(double) * nd);
+    double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+    double* o = (double*)malloc(sizeof(double) * (size_t)D * 3);
+    if (!a || !ah || !kx || !kh || !vx || !vh || !qr || !o) {
+        free(a); free(ah); free(kx); free(kh); free(vx); free(vh); free(qr); free(o);
+        return -2;
+    }
+    int group = hq / hkv;
+    for (int r = row_begin; r < row_end; ++r) {
+        int b = r / hq, h = r % hq, kvh = h / group;
+        size_t bh = (size_t)b * hkv + kvh;
+        double* m = rows_out + (size_t)(r - row_begin) * 6;
+        for (int i = 0; i < 6; ++i)
+            m[i] = 0.0;
+        for (int t = 0; t < n; ++t) {
+            stored_row(kpt, 0, k_codes, k_meta, k_tail, k_sink, dtype, bh, t, n,
+                       D, G, kbits, R, S, gcap, tcap, kh + (size_t)t * D);
+            stored_row(vpt, R > 0, v_codes, v_meta, v_tail, v_sink, dtype, bh, t,
+                       n, D, G, vbits, R, S, gcap, tcap, vh + (size_t)t * D);
+            for (int c = 0; c < D; ++c) {
+                size_t i = (size_t)t * D + c;
+                kx[i] = load_elem(k, dtype, (bh * n + t) * D + c);
+                vx[i] = load_elem(v, dtype, (bh * n + t) * D + c);
+                m[4] += (kh[i] - kx[i]) * (kh[i] - kx[i]);
+                m[5] += (vh[i] - vx[i]) * (vh[i] - vx[i]);
+            }
+        }
+        for (int c = 0; c < D; ++c)
+            qr[c] = load_elem(q, dtype, (size_t)r * D + c);
+        orc_rope(qr, D, (double)(n - 1), base);
+        for (int t = 0; t < n; ++t) {
+            orc_rope(kx + (size_t)t * D, D, (double)t, base);
+            orc_rope(kh + (size_t)t * D, D, (double)t, base);
+            double d0 = 0.0, d1 = 0.0;
+            for (int c = 0; c < D; ++c) {
+                d0 += qr[c] * kx[(size_t)t * D + c];
+                d1 += qr[c] * kh[(size_t)t * D + c];
+            }
+            a[t] = d0 / sqrt((double)D);
+            ah[t] = d1 / sqrt((double)D);
+        }
+        softmax_weights(a, n);
+        softmax_weights(ah, n);
+        for (int i = 0; i < 3 * D; ++i)
+            o[i] = 0.0;
+        for (int t = 0; t < n; ++t) {
+            m[0] += (ah[t] - a[t]) * (ah[t] - a[t]);
+            for (int c = 0; c < D; ++c) {
+                size_t i = (size_t)t * D + c;
+                o[c] += a[t] * vx[i];          /* reference */
+                o[D + c] += a[t] * vh[i];      /* stored values */
+                o[2 * D + c] += ah[t] * vh[i]; /* end to end */
+            }
+        }
+        for (int c = 0; c < D; ++c) {
+            m[1] += (o[D + c] - o[c]) * (o[D + c] - o[c]);
+            m[2] += o[c] * o[c];
+            m[3] += (o[2 * D + c] - o[c]) * (o[2 * D + c] - o[c]);
+        }
+    }
+    free(a); free(ah); free(kx); free(kh); free(vx); free(vh); free(qr); free(o);
     return 0;
 }

@@ -13,6 +13,11 @@ fraction of larger tokens.  The pages' own measurements come from trained
 models (Llama-2-7B/13B) that are not available here; these seeded draws stand
 in for them.
 
+The geometry ablation uses a second key recipe ("steady"): the outlier
+channels keep a fixed sign and a large magnitude with a small spread across
+tokens (factor * (sign + 0.25 * N(0, 1))), the page's picture of channels that
+carry very large magnitudes consistently across every token.
+
 Random access: every (sequence, 256-token block) has its own generator,
 seeded by ``SeedSequence([seed, stream, sequence, block])``, and tokens are
 drawn token-major, so token t of sequence b has the same value whatever range
@@ -25,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 BLOCK = 256
-_S_KEYS, _S_VALS, _S_VOUT, _S_QUERY, _S_KOUT = 1, 2, 3, 4, 5
+_S_KEYS, _S_VALS, _S_VOUT, _S_QUERY, _S_KOUT, _S_KSIGN = 1, 2, 3, 4, 5, 6
 
 
 @dataclass(frozen=True)
@@ -39,7 +44,7 @@ class Config:
     key_bits: int
     value_bits: int
     dtype: str                 # "float16" | "float32"
-    key_recipe: str            # "tiny" | "u20_100" | "x50"
+    key_recipe: str            # "tiny" | "u20_100" | "x50" | "steady"
     value_outliers: bool       # 1 % of tokens x5
     group: int = 32
     rope_base: float = 10000.0
@@ -75,6 +80,11 @@ CONFIGS = {
         "long", 1, 32, 32, 128, 131072, 4, 2, "float16", "x50", False,
         description="long context: batch 1, 32 heads, head_dim 128, 131072 "
                     "tokens, fp16, keys B=4, values B=2"),
+    "ablation_7b": Config(
+        "ablation_7b", 8, 32, 32, 128, 4096, 2, 2, "float16", "steady", True,
+        description="geometry ablation on the Llama-2-7B shape: batch 8, 32 heads, "
+                    "head_dim 128, 4096 tokens, fp16, B=2, G=32; outlier key "
+                    "channels of steady sign and magnitude"),
     "gqa": Config(
         "gqa", 64, 32, 8, 128, 16384, 2, 2, "float16", "u20_100", True,
         description="Llama-3-8B-shaped GQA: batch 64, 32 query heads over 8 KV "
@@ -102,6 +112,12 @@ def key_outliers(cfg: Config, seed: int = 0):
     return ch, f
 
 
+def key_outlier_signs(cfg: Config, seed: int = 0):
+    """Signs (+-1, float32[Hkv][m]) of the steady outlier channels."""
+    ch, _ = key_outliers(cfg, seed)
+    return _rng(seed, _S_KSIGN).choice(np.array([-1.0, 1.0], dtype=np.float32), size=ch.shape)
+
+
 def _block_tokens(cfg, seed, stream, b, blk):
     rng = _rng(seed, stream, b, blk)
     return rng.standard_normal((BLOCK, cfg.kv_heads, cfg.head_dim), dtype=np.float32)
@@ -126,9 +142,13 @@ def make_keys(cfg: Config, seed: int = 0, t0: int = 0, t1=None, seqs=None):
     t1 = cfg.n_tokens if t1 is None else t1
     k = _draw(cfg, seed, _S_KEYS, t0, t1, seqs)
     ch, f = key_outliers(cfg, seed)
+    sg = key_outlier_signs(cfg, seed) if cfg.key_recipe == "steady" else None
     for h in range(cfg.kv_heads):
         for m in range(ch.shape[1]):
-            k[:, h, :, ch[h, m]] *= f[h, m]
+            if sg is None:
+                k[:, h, :, ch[h, m]] *= f[h, m]
+            else:
+                k[:, h, :, ch[h, m]] = f[h, m] * (sg[h, m] + 0.25 * k[:, h, :, ch[h, m]])
     return k.astype(cfg.np_dtype)
 
 
