@@ -80,22 +80,40 @@ def quantized_tokens(n: int, G: int, residual: int, sink: int = 0) -> int:
     return max(q, min(n, sink))
 
 
-def attend_bytes(cfg, n: int, residual: int = 0, sink: int = 0) -> int:
-    """Algorithmic bytes of one decode-attention call at length n: packed key
-    codes + key meta + unquantized keys + value codes + value meta (+
-    unquantized values of the windows) + q + out."""
+GEOMETRIES = {"kivi": 0, "keys_per_token": 1, "values_per_channel": 2, "both_flipped": 3}
+
+
+def cache_bytes(cfg, n: int, residual: int = 0, sink: int = 0, geometry: int = 0) -> int:
+    """Bytes a cache of n tokens holds for the attention to read: per
+    operand, packed codes and binary16 (step, zero) pairs of the quantized
+    tokens and the unquantized rows of the others.  Keys grouped per channel
+    (the default) have one meta word per (group of G tokens, channel), keys
+    grouped per token one per (token, group of G channels); the same for
+    values.  Windows: tokens [min(n, S), Tq) are quantized (values [S, n)
+    without a residual window); a flipped geometry has no windows, an
+    operand grouped per token is fully quantized and one grouped per channel
+    up to G * floor(n / G)."""
     G, D = cfg.group, cfg.head_dim
     nbh = cfg.batch * cfg.kv_heads
     esz = 2 if cfg.dtype == "float16" else 4
     ns = min(n, sink)
     tq = quantized_tokens(n, G, residual, sink)
-    vq = tq if residual > 0 else n
-    kq, vqn = tq - ns, vq - ns  # quantized key and value tokens
-    return (nbh * kq * D * cfg.key_bits // 8 + nbh * (kq // G) * D * 4
-            + nbh * (n - kq) * D * esz
-            + nbh * vqn * D * cfg.value_bits // 8 + nbh * vqn * (D // G) * 4
-            + nbh * (n - vqn) * D * esz
-            + cfg.batch * cfg.q_heads * D * esz + cfg.batch * cfg.q_heads * D * 4)
+    key_tok, val_tok = bool(geometry & 1), not geometry & 2
+    kq = n if key_tok else tq - ns
+    vq = (tq if residual > 0 else n) - ns if val_tok else tq
+
+    def operand(bits, nq, per_token):
+        meta = nq * (D // G) if per_token else (nq // G) * D
+        return nbh * (nq * D * bits // 8 + meta * 4 + (n - nq) * D * esz)
+
+    return operand(cfg.key_bits, kq, key_tok) + operand(cfg.value_bits, vq, val_tok)
+
+
+def attend_bytes(cfg, n: int, residual: int = 0, sink: int = 0, geometry: int = 0) -> int:
+    """Algorithmic bytes of one decode-attention call at length n: the
+    cache's planes and unquantized rows, q and out."""
+    return (cache_bytes(cfg, n, residual, sink, geometry)
+            + cfg.batch * cfg.q_heads * cfg.head_dim * ((2 if cfg.dtype == "float16" else 4) + 4))
 
 
 def attend_flops(cfg, n: int) -> int:
@@ -107,20 +125,11 @@ def attend_flops(cfg, n: int) -> int:
     return cfg.batch * cfg.kv_heads * n * cfg.head_dim * (7 + 4 * qpk)
 
 
-def prefill_bytes(cfg, n: int, residual: int = 0, sink: int = 0) -> int:
+def prefill_bytes(cfg, n: int, residual: int = 0, sink: int = 0, geometry: int = 0) -> int:
     """Quantize-and-pack of n tokens: K and V read once, planes written."""
-    G, D = cfg.group, cfg.head_dim
-    nbh = cfg.batch * cfg.kv_heads
     esz = 2 if cfg.dtype == "float16" else 4
-    ns = min(n, sink)
-    tq = quantized_tokens(n, G, residual, sink)
-    vq = tq if residual > 0 else n
-    kq, vqn = tq - ns, vq - ns
-    return (2 * nbh * n * D * esz
-            + nbh * kq * D * cfg.key_bits // 8 + nbh * (kq // G) * D * 4
-            + nbh * (n - kq) * D * esz
-            + nbh * vqn * D * cfg.value_bits // 8 + nbh * vqn * (D // G) * 4
-            + nbh * (n - vqn) * D * esz)
+    return (2 * cfg.batch * cfg.kv_heads * n * cfg.head_dim * esz
+            + cache_bytes(cfg, n, residual, sink, geometry))
 
 
 class HipEvents:
@@ -161,7 +170,8 @@ class HipEvents:
         self.ev = []
 
 
-def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0, sink: int = 0):
+def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0, sink: int = 0,
+                 geometry: int = 0):
     """The oracle (plain single-threaded fp64 C) on a bounded sample of the
     same workload: decode attention for whole sequences, rows timed until
     about budget_s seconds of CPU work."""
@@ -176,22 +186,32 @@ def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0, sink: i
     q = synth.make_query(cfg, 0, 0)
     rows_done, t_total, bytes_done = 0, 0.0, 0
     one = synth.scaled(cfg, batch=1)
-    per_row = attend_bytes(one, n, residual, sink) / cfg.q_heads
+    per_row = attend_bytes(one, n, residual, sink, geometry) / cfg.q_heads
     for b in range(cfg.batch):
         k = synth.make_keys(cfg, 0, 0, n, seqs=[b])
         v = synth.make_values(cfg, 0, 0, n, seqs=[b])
-        kp = oracle.quantize_keys(k, cfg.key_bits, cfg.group, residual=residual, sink=sink)
-        vals = oracle.quantize_values(v, cfg.value_bits, cfg.group, residual=residual, sink=sink)
-        pl = dict(k_codes=kp[0], k_meta=kp[1], k_tail=kp[2], v_codes=vals[0], v_meta=vals[1])
-        if residual > 0:
-            pl["v_tail"] = vals[2]
-        if sink > 0:
-            pl["k_sink"], pl["v_sink"] = kp[3], vals[-1]
+        if geometry:
+            pl = oracle.geometry_planes(k, v, cfg.key_bits, cfg.value_bits, geometry, cfg.group)
+        else:
+            kp = oracle.quantize_keys(k, cfg.key_bits, cfg.group, residual=residual, sink=sink)
+            vals = oracle.quantize_values(v, cfg.value_bits, cfg.group, residual=residual,
+                                          sink=sink)
+            pl = dict(k_codes=kp[0], k_meta=kp[1], k_tail=kp[2], v_codes=vals[0],
+                      v_meta=vals[1])
+            if residual > 0:
+                pl["v_tail"] = vals[2]
+            if sink > 0:
+                pl["k_sink"], pl["v_sink"] = kp[3], vals[-1]
         for r in range(cfg.q_heads):
             t0 = time.perf_counter()
-            oracle.attend(pl, q[b:b + 1], n, cfg.key_bits, cfg.value_bits, cfg.kv_heads,
-                          cfg.group, cfg.rope_base, rows=(r, r + 1), residual=residual,
-                          sink=sink)
+            if geometry:
+                oracle.attend_geometry(pl, q[b:b + 1], n, cfg.key_bits, cfg.value_bits,
+                                       cfg.kv_heads, geometry, cfg.group, cfg.rope_base,
+                                       rows=(r, r + 1))
+            else:
+                oracle.attend(pl, q[b:b + 1], n, cfg.key_bits, cfg.value_bits, cfg.kv_heads,
+                              cfg.group, cfg.rope_base, rows=(r, r + 1), residual=residual,
+                              sink=sink)
             t_total += time.perf_counter() - t0
             rows_done += 1
             bytes_done += per_row
@@ -223,6 +243,10 @@ def main():
                     help="recent tokens kept in full precision (a multiple of 32)")
     ap.add_argument("--sink", type=int, default=0,
                     help="first tokens kept in full precision (a multiple of 32)")
+    ap.add_argument("--geometry", default="kivi", choices=sorted(GEOMETRIES),
+                    help="grouping axes (the ablation flips keys and/or values; no windows)")
+    ap.add_argument("--no-metrics", action="store_true",
+                    help="skip the error-where-consumed metrics of the prompt cache")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
@@ -251,8 +275,9 @@ def main():
     total_steps = args.warmup + args.steps
 
     Rw, Sw = args.residual, args.sink
-    cache_bytes = attend_bytes(cfg, n, Rw, Sw)
-    R = args.caches or max(2, math.ceil(2 * INFINITY_CACHE / cache_bytes) + 1)
+    geom = GEOMETRIES[args.geometry]
+    one_cache = attend_bytes(cfg, n, Rw, Sw, geom)
+    R = args.caches or max(2, math.ceil(2 * INFINITY_CACHE / one_cache) + 1)
     visits = math.ceil(total_steps / R)
     max_tokens = n + visits
 
@@ -268,7 +293,7 @@ def main():
 
     caches = [QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
                                cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev,
-                               residual=Rw, sink=Sw)
+                               residual=Rw, sink=Sw, geometry=geom)
               for _ in range(R)]
     # prefill (quantize-and-pack of the whole prompt), timed per cache after
     # one untimed prefill of a one-group cache (first launches load the code)
@@ -285,6 +310,17 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         pf_ms.append(e0.elapsed_time(e1))
+    # error where it is consumed, on the first cache's prompt (before the
+    # appends): the unquantized prompt keys and values are still at hand
+    metrics = None
+    if not args.no_metrics:
+        q_prompt = torch.from_numpy(synth.make_query(cfg, 0, 0)).to(dev)
+        mv = caches[0].error_metrics(k, v, q_prompt).cpu().numpy()
+        metrics = {name: float(x) for name, x in zip(
+            ("key_error", "score_error", "value_error", "value_output_rel_error",
+             "output_rel_error"), mv)}
+        metrics["tokens"] = n - 1
+        del q_prompt
     del k, v
     torch.cuda.synchronize()
 
@@ -333,7 +369,7 @@ def main():
         raise RuntimeError("cache lengths do not match the steps issued")
 
     wall = t1 - t0
-    total_bytes = sum(attend_bytes(cfg, L, Rw, Sw) for L in lengths)
+    total_bytes = sum(attend_bytes(cfg, L, Rw, Sw, geom) for L in lengths)
     value = total_bytes / wall / 1e9
     attend_ms = np.array([hev.elapsed_ms(2 * j, 2 * j + 1) for j in range(args.steps)])
     hev.close()
@@ -363,6 +399,7 @@ def main():
             "value_bits": cfg.value_bits, "group": cfg.group, "kv_dtype": cfg.dtype,
             "residual": Rw,
             "sink": Sw,
+            "geometry": args.geometry,
             "context_during_steps": [min(lengths), max(lengths)],
             "rotating_caches": R,
             "parallelism": "single GPU",
@@ -375,9 +412,11 @@ def main():
             "peak": FP32_VECTOR_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(cfg.name) if Rw == 0 and Sw == 0 else None,
-            "kernel": "attend_kernel (decode attention); HIP events around each "
-                      "kvq_attend_decode call in the timed loop",
+            "traffic": (measured_traffic(cfg.name) if Rw == 0 and Sw == 0 and geom == 0
+                        else None),
+            "kernel": ("attend_kernel (decode attention)" if geom == 0 else
+                       "attend_geometry_kernel (geometry ablation attention)")
+                      + "; HIP events around each kvq_attend_decode call in the timed loop",
             "flops_per_launch": int(flops_per_launch),
             "bytes_per_launch": int(bytes_per_launch),
             "avg_launch_us": round(att_avg_s * 1e6, 3),
@@ -389,15 +428,17 @@ def main():
         "prefill": {
             "tokens": n - 1,
             "median_ms": round(float(np.median(pf_ms)), 4),
-            "GB_per_s": round(prefill_bytes(cfg, n - 1, Rw, Sw) / (np.median(pf_ms) / 1e3) / 1e9,
-                              2),
+            "GB_per_s": round(prefill_bytes(cfg, n - 1, Rw, Sw, geom)
+                              / (np.median(pf_ms) / 1e3) / 1e9, 2),
             "tokens_per_s": round(cfg.batch * (n - 1) / (np.median(pf_ms) / 1e3), 1),
         },
     }
+    if metrics is not None:
+        res["error_metrics"] = metrics
     for c in caches:
         c.close()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, n, residual=Rw, sink=Sw)
+        res["cpu_baseline"] = cpu_baseline(cfg, n, residual=Rw, sink=Sw, geometry=geom)
     print(json.dumps(res), flush=True)
 
 

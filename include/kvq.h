@@ -73,6 +73,19 @@
  * first tokens in high precision): keys and values of tokens [0, min(n, S))
  * stay unquantized for good, quantization starts at token S, and Tq above is
  * raised to at least min(n, S).
+ * Geometry ablation, kvq_config.geometry (the page "Your KV Cache Doesn't Have
+ * a Bit Problem...", lede and sections "Keys: The Outliers Live in Fixed
+ * Channels" and "Values: Where the Intuition Breaks": the same bits spent
+ * along the other axis).  0 is the layout above.  KVQ_KEYS_PER_TOKEN groups
+ * keys like values (G channels of one token, quantized on arrival): K_CODES
+ * is u32[batch][kv_heads][Tcap][head_dim/G][Wk] and K_META
+ * u32[batch][kv_heads][Tcap][head_dim/G], and the key tail is unused.
+ * KVQ_VALUES_PER_CHANNEL groups values like keys (one channel over G
+ * tokens): V_CODES is u32[batch][kv_heads][Gcap][head_dim][Wv], V_META
+ * u32[batch][kv_heads][Gcap][head_dim], and value tokens t >= G*floor(n/G)
+ * wait verbatim in V_TAIL (G slots, token t in slot t mod G) until their
+ * group fills.  Plane sizes do not change.  A non-zero geometry requires
+ * residual == sink == 0; its attention runs in a separate, plain kernel.
  * The step and zero are each rounded once, to nearest-even, from the exact
  * value (range/(2^B-1) and the minimum); the code of x is the integer nearest
  * to (x - zero)/step computed exactly, ties to even, clamped to
@@ -107,6 +120,19 @@ enum {
 
 enum { KVQ_F16 = 0, KVQ_F32 = 1 };
 
+/* kvq_config.geometry bits (0 = keys per channel, values per token). */
+enum { KVQ_KEYS_PER_TOKEN = 1, KVQ_VALUES_PER_CHANNEL = 2 };
+
+/* Entries of the kvq_error_metrics result. */
+enum {
+    KVQ_METRIC_KEY_ERROR = 0,
+    KVQ_METRIC_SCORE_ERROR = 1,
+    KVQ_METRIC_VALUE_ERROR = 2,
+    KVQ_METRIC_VALUE_OUTPUT_REL_ERROR = 3,
+    KVQ_METRIC_OUTPUT_REL_ERROR = 4,
+    KVQ_METRICS = 5
+};
+
 typedef struct kvq_config {
     int32_t batch;      /* sequences, >= 1                                  */
     int32_t q_heads;    /* query heads, multiple of kv_heads                */
@@ -122,6 +148,8 @@ typedef struct kvq_config {
                            multiple of group in [0, 1024]; 0 = none         */
     int32_t sink;       /* S: first tokens kept in full precision, a
                            multiple of group in [0, 1024]; 0 = none         */
+    int32_t geometry;   /* 0, or KVQ_KEYS_PER_TOKEN | KVQ_VALUES_PER_CHANNEL
+                           (ablation; needs residual == sink == 0)          */
 } kvq_config;
 
 typedef struct kvq_layout {
@@ -157,7 +185,9 @@ int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes,
  * per channel (K_CODES, K_META) and keys t >= Tq go to the K_TAIL ring;
  * R = 0: every value token t >= S is quantized per channel group (V_CODES,
  * V_META); R > 0: values S <= t < Tq are quantized and values t >= Tq go to
- * the V_TAIL ring.  Sets n = n_tokens.
+ * the V_TAIL ring.  A non-zero geometry quantizes every token of an operand
+ * grouped per token, and the groups g < n_tokens/G of one grouped per
+ * channel (the rest to its tail).  Sets n = n_tokens.
  * n_tokens == 0 is allowed and enqueues nothing.
  * Errors: KVQ_ERR_ARG (null handle or pointers with n_tokens > 0, negative
  * n_tokens), KVQ_ERR_STATE (n != 0), KVQ_ERR_CAPACITY (n_tokens >
@@ -166,7 +196,10 @@ int kvq_quantize_prefill(kvq_t* h, const void* d_k, const void* d_v,
                          int32_t n_tokens, void* stream);
 
 /* Append one token per sequence: d_k, d_v are dtype[batch][kv_heads]
- * [head_dim].  While n < S key and value go to sink slot n.  Otherwise,
+ * [head_dim].  With a non-zero geometry, an operand grouped per token is
+ * quantized at once and one grouped per channel goes to tail slot n mod G,
+ * its group quantized when n+1 is a multiple of G.  Otherwise:
+ * while n < S key and value go to sink slot n.  Otherwise,
  * R = 0: the value is quantized at once; the key goes to tail
  * slot n mod G, and when that fills the tail (n+1 a multiple of G) the G
  * tail keys are quantized as key group n/G in the same launch.  R > 0: key
@@ -186,6 +219,29 @@ int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v,
  * concurrently.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (n == 0), KVQ_ERR_HIP. */
 int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream);
+
+/* Error where it is consumed (the page "Your KV Cache Doesn't Have a Bit
+ * Problem...", sections "Keys: The Outliers Live in Fixed Channels" and
+ * "Values: Where the Intuition Breaks": validate on attention, not on the
+ * stored tensor), computed in fp64 for the current cache of n tokens.
+ * d_k, d_v: dtype[batch][kv_heads][n][head_dim], the unquantized keys
+ * (before the rotary embedding) and values of all n cached tokens, i.e.
+ * what prefill and the appends received, in order.  d_q: as for
+ * kvq_attend_decode.  d_metrics: double[KVQ_METRICS], each entry a mean over
+ * the batch * q_heads output rows; with a = softmax of the scores from the
+ * unquantized keys, ahat the same from the stored keys (dequantized codes,
+ * or the verbatim tail, ring and sink rows), vhat the stored values:
+ *   KEY_ERROR               Frobenius norm of khat - k over the row's KV head
+ *                           (before the rotation);
+ *   SCORE_ERROR             L2 norm of ahat - a;
+ *   VALUE_ERROR             Frobenius norm of vhat - v over the row's KV head;
+ *   VALUE_OUTPUT_REL_ERROR  |sum_t a_t vhat_t - sum_t a_t v_t| / |sum_t a_t v_t|;
+ *   OUTPUT_REL_ERROR        |sum_t ahat_t vhat_t - sum_t a_t v_t| / |sum_t a_t v_t|.
+ * Uses the workspace's partials region as scratch (like kvq_attend_decode:
+ * not concurrently with another attend or metrics call on the handle).
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (n == 0), KVQ_ERR_HIP. */
+int kvq_error_metrics(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
+                      double* d_metrics, void* stream);
 
 /* Free the handle (host memory only; the workspace is untouched).
  * Errors: KVQ_ERR_ARG (null). */

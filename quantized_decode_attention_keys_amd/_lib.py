@@ -20,6 +20,16 @@ KVQ_ERR_HIP = -6
 KVQ_F16 = 0
 KVQ_F32 = 1
 
+KVQ_KEYS_PER_TOKEN = 1
+KVQ_VALUES_PER_CHANNEL = 2
+
+KVQ_METRIC_KEY_ERROR = 0
+KVQ_METRIC_SCORE_ERROR = 1
+KVQ_METRIC_VALUE_ERROR = 2
+KVQ_METRIC_VALUE_OUTPUT_REL_ERROR = 3
+KVQ_METRIC_OUTPUT_REL_ERROR = 4
+KVQ_METRICS = 5
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -48,6 +58,7 @@ class KvqConfig(ctypes.Structure):
         ("rope_base", ctypes.c_float),
         ("residual", ctypes.c_int32),
         ("sink", ctypes.c_int32),
+        ("geometry", ctypes.c_int32),
     ]
 
 
@@ -98,6 +109,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_append_token.restype = ctypes.c_int
         L.kvq_attend_decode.argtypes = [P, P, P, P]
         L.kvq_attend_decode.restype = ctypes.c_int
+        L.kvq_error_metrics.argtypes = [P, P, P, P, P, P]
+        L.kvq_error_metrics.restype = ctypes.c_int
         L.kvq_destroy.argtypes = [P]
         L.kvq_destroy.restype = ctypes.c_int
         L.kvq_length.argtypes = [P]
@@ -144,6 +157,11 @@ def kvq_append_token(h: int, d_k: int, d_v: int, stream: int) -> int:
 
 def kvq_attend_decode(h: int, d_q: int, d_out: int, stream: int) -> int:
     return lib().kvq_attend_decode(h, d_q, d_out, stream)
+
+
+def kvq_error_metrics(h: int, d_k: int, d_v: int, d_q: int, d_metrics: int,
+                      stream: int) -> int:
+    return lib().kvq_error_metrics(h, d_k, d_v, d_q, d_metrics, stream)
 
 
 def kvq_destroy(h: int) -> int:

@@ -23,18 +23,19 @@ class QuantizedKVCache:
     contiguous tensors of `dtype` on the cache's device; keys and queries are
     before the rotary embedding.  `residual` keeps the most recent tokens
     (at least `residual`, fewer than `residual` + group) in full precision,
-    `sink` the first `sink` tokens.
+    `sink` the first `sink` tokens.  `geometry` (ablation, no windows) flips
+    the grouping axis: KVQ_KEYS_PER_TOKEN and/or KVQ_VALUES_PER_CHANNEL.
     Calls enqueue on the current torch stream (or `stream`) and return at
     once."""
 
     def __init__(self, batch, q_heads, kv_heads, head_dim, max_tokens, key_bits=2,
                  value_bits=2, dtype=torch.float16, rope_base=10000.0, group=32,
-                 device=None, residual=0, sink=0):
+                 device=None, residual=0, sink=0, geometry=0):
         if dtype not in _DTYPES:
             raise TypeError("dtype must be torch.float16 or torch.float32")
         self.cfg = L.KvqConfig(batch, q_heads, kv_heads, head_dim, max_tokens, group,
                                key_bits, value_bits, _DTYPES[dtype], rope_base, residual,
-                               sink)
+                               sink, geometry)
         self.dtype = dtype
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
             else torch.device(device)
@@ -93,6 +94,23 @@ class QuantizedKVCache:
                "kvq_attend_decode")
         return out
 
+    def error_metrics(self, k, v, q, stream=None):
+        """Error where it is consumed for the current cache: k, v are the
+        unquantized keys and values of all cached tokens
+        ([batch][kv_heads][n][head_dim]), q as for `attend`.  Returns a float64
+        tensor of KVQ_METRICS entries on the device (key, score, value,
+        value-output and output error; see kvq.h)."""
+        c = self.cfg
+        n = len(self)
+        shape = (c.batch, c.kv_heads, n, c.head_dim)
+        pk = self._arg(k, shape, "k")
+        pv = self._arg(v, shape, "v")
+        pq = self._arg(q, (c.batch, c.q_heads, c.head_dim), "q")
+        out = torch.empty(L.KVQ_METRICS, dtype=torch.float64, device=self.device)
+        _check(L.kvq_error_metrics(self.handle, pk, pv, pq, out.data_ptr(),
+                                   self._stream(stream)), "kvq_error_metrics")
+        return out
+
     def planes(self):
         """Views of the packed planes inside the workspace (no copy)."""
         c, lay = self.cfg, self.layout
@@ -108,14 +126,20 @@ class QuantizedKVCache:
             esz = torch.tensor([], dtype=dt).element_size()
             return ws[off:off + n * esz].view(dt).view(shape)
 
+        by_token = lambda w: (nb, h, lay.tcap, D // G, w)  # noqa: E731
+        by_channel = lambda w: (nb, h, lay.gcap, D, w)  # noqa: E731
+        kpt = bool(c.geometry & L.KVQ_KEYS_PER_TOKEN)
+        vpc = bool(c.geometry & L.KVQ_VALUES_PER_CHANNEL)
+        ks = by_token(wk) if kpt else by_channel(wk)
+        vs = by_channel(wv) if vpc else by_token(wv)
         return {
-            "k_codes": view(lay.k_codes, (nb, h, lay.gcap, D, wk), torch.int32),
-            "k_meta": view(lay.k_meta, (nb, h, lay.gcap, D), torch.int32),
-            "v_codes": view(lay.v_codes, (nb, h, lay.tcap, D // G, wv), torch.int32),
-            "v_meta": view(lay.v_meta, (nb, h, lay.tcap, D // G), torch.int32),
+            "k_codes": view(lay.k_codes, ks, torch.int32),
+            "k_meta": view(lay.k_meta, ks[:-1], torch.int32),
+            "v_codes": view(lay.v_codes, vs, torch.int32),
+            "v_meta": view(lay.v_meta, vs[:-1], torch.int32),
             "k_tail": view(lay.k_tail, (nb, h, lay.tail_slots, D), self.dtype),
-            "v_tail": view(lay.v_tail, (nb, h, lay.tail_slots if c.residual > 0 else 0, D),
-                           self.dtype),
+            "v_tail": view(lay.v_tail, (nb, h, lay.tail_slots if c.residual > 0 or vpc else 0,
+                                        D), self.dtype),
             "k_sink": view(lay.k_sink, (nb, h, c.sink, D), self.dtype),
             "v_sink": view(lay.v_sink, (nb, h, c.sink, D), self.dtype),
         }

@@ -35,14 +35,16 @@ int check_config(const kvq_config* c)
     if (c->batch < 1 || c->q_heads < 1 || c->kv_heads < 1 || c->head_dim < 1 ||
         c->max_tokens < 1 || c->group < 1 || c->key_bits < 1 || c->value_bits < 1 ||
         !(c->rope_base > 1.0f) || !std::isfinite(c->rope_base) || c->q_heads % c->kv_heads != 0 ||
-        (c->dtype != KVQ_F16 && c->dtype != KVQ_F32) || c->residual < 0 || c->sink < 0)
+        (c->dtype != KVQ_F16 && c->dtype != KVQ_F32) || c->residual < 0 || c->sink < 0 ||
+        c->geometry < 0 || c->geometry > (KVQ_KEYS_PER_TOKEN | KVQ_VALUES_PER_CHANNEL))
         return KVQ_ERR_ARG;
     const int qpk = c->q_heads / c->kv_heads;
     if (c->group != kvqi::kGroup || (c->head_dim != 64 && c->head_dim != 128) ||
         (c->key_bits != 2 && c->key_bits != 4 && c->key_bits != 8) ||
         (c->value_bits != 2 && c->value_bits != 4 && c->value_bits != 8) ||
         (qpk != 1 && qpk != 2 && qpk != 4 && qpk != 8) || c->residual % kvqi::kGroup != 0 ||
-        c->residual > kMaxResidual || c->sink % kvqi::kGroup != 0 || c->sink > kMaxResidual)
+        c->residual > kMaxResidual || c->sink % kvqi::kGroup != 0 || c->sink > kMaxResidual ||
+        (c->geometry != 0 && (c->residual != 0 || c->sink != 0)))
         return KVQ_ERR_UNSUPPORTED;
     // keep every plane index inside 2^31 elements per (sequence, head) and
     // the grid dimensions inside their limits
@@ -71,7 +73,8 @@ void make_layout(const kvq_config* c, kvq_layout* L)
     L->v_meta = off;    off = align_up(off + nb * hkv * tcap * (D / G) * 4);
     const size_t ring = (size_t)c->residual + G;
     L->k_tail = off;    off = align_up(off + nb * hkv * ring * D * esz);
-    L->v_tail = off;    off = align_up(off + (c->residual > 0 ? nb * hkv * ring * D * esz : 0));
+    const bool v_ring = c->residual > 0 || (c->geometry & KVQ_VALUES_PER_CHANNEL) != 0;
+    L->v_tail = off;    off = align_up(off + (v_ring ? nb * hkv * ring * D * esz : 0));
     L->k_sink = off;    off = align_up(off + nb * hkv * (size_t)c->sink * D * esz);
     L->v_sink = off;    off = align_up(off + nb * hkv * (size_t)c->sink * D * esz);
     L->rope_group = off; off = align_up(off + (size_t)gcap * (D / 2) * 8);
@@ -112,6 +115,8 @@ kvqi::Planes planes_of(const kvq* h)
     p.residual = h->cfg.residual;
     p.ring = L.tail_slots;
     p.sink = h->cfg.sink;
+    p.geometry = h->cfg.geometry;
+    p.rope_base = h->cfg.rope_base;
     return p;
 }
 
@@ -295,13 +300,34 @@ int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream)
     if (h->n == 0)
         return KVQ_ERR_STATE;
     const int n = h->n;
-    int splits, waves;
-    attend_shape(h, n, &splits, &waves);
     const kvqi::Planes p = planes_of(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (h->cfg.geometry != 0) {
+        // about kTargetBlocks blocks, at least one 32-token chunk per split
+        const int rows = h->cfg.batch * h->cfg.q_heads;
+        const int chunks = (n + h->cfg.group - 1) / h->cfg.group;
+        int splits = (kTargetBlocks + rows - 1) / rows;
+        if (splits > chunks) splits = chunks;
+        if (splits > h->layout.max_splits) splits = h->layout.max_splits;
+        if (splits < 1) splits = 1;
+        return hip_status(kvqi::launch_attend_geometry(p, d_q, d_out, n, splits, s));
+    }
+    int splits, waves;
+    attend_shape(h, n, &splits, &waves);
     return hip_status(h->cfg.head_dim == 64
                           ? kvqi::launch_attend_d64(p, d_q, d_out, n, splits, waves, s)
                           : kvqi::launch_attend_d128(p, d_q, d_out, n, splits, waves, s));
+}
+
+int kvq_error_metrics(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
+                      double* d_metrics, void* stream)
+{
+    if (!h || !d_k || !d_v || !d_q || !d_metrics)
+        return KVQ_ERR_ARG;
+    if (h->n == 0)
+        return KVQ_ERR_STATE;
+    return hip_status(kvqi::launch_error_metrics(planes_of(h), d_k, d_v, d_q, d_metrics, h->n,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int kvq_destroy(kvq_t* h)

@@ -34,7 +34,15 @@ struct Planes {
     int nb, hq, hkv, D, kbits, vbits, gcap, tcap, max_splits, dtype;
     int residual, ring;  // R and R + G
     int sink;            // S
+    int geometry;        // 0, or kKeysPerToken | kValuesPerChannel (then R = S = 0)
+    double rope_base;    // theta_i = rope_base^(-2i/D) (fp64 paths recompute angles)
 };
+
+// Geometry ablation bits: keys grouped like values (G channels of one token,
+// planes [tcap][D/G][wk]) and values grouped like keys (one channel over G
+// tokens, planes [gcap][D][wv], unfilled groups in v_tail).
+constexpr int kKeysPerToken = 1;
+constexpr int kValuesPerChannel = 2;
 
 // Tq: tokens [0, Tq) of an n-token cache are quantized (keys in whole
 // groups); the keys of [Tq, n), and with a residual window its values, are
@@ -64,5 +72,12 @@ hipError_t launch_attend_d64(const Planes& p, const void* q, float* out, int n,
                              int splits, int waves, hipStream_t stream);
 hipError_t launch_attend_d128(const Planes& p, const void* q, float* out, int n,
                               int splits, int waves, hipStream_t stream);
+// Attention over a cache with a non-zero geometry (kvq_geometry.hip).
+hipError_t launch_attend_geometry(const Planes& p, const void* q, float* out, int n,
+                                  int splits, hipStream_t stream);
+// Error where it is consumed: fp64, any geometry and windows; uses the
+// partials region as scratch for per-row sums (kvq_geometry.hip).
+hipError_t launch_error_metrics(const Planes& p, const void* k, const void* v, const void* q,
+                                double* metrics, int n, hipStream_t stream);
 
 }  // namespace kvqi

@@ -115,20 +115,76 @@ __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __
     p.v_meta[tc] = meta;
 }
 
+// Append one token of an operand grouped per token (G channels of one
+// token row) at cache slot n: thread c = channel c of the row.  The 32 lanes
+// of a channel group find the group's min and max with lane shuffles, each
+// codes its own element, and the codes are OR-reduced into 32-bit words
+// across the lanes that share a word.  Every lane of the block must call it.
+template <typename T, int BITS>
+__device__ __forceinline__ void append_token_groups(uint32_t* __restrict__ codes,
+                                                    uint32_t* __restrict__ meta, int tcap,
+                                                    const T* __restrict__ row, size_t bh, int n,
+                                                    int c, int D)
+{
+    constexpr int CPW = 32 / BITS;  // codes per 32-bit word
+    const float x = to_f32(row[c]);
+    float mn = x, mx = x;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) {  // within the 32-lane group
+        mn = fminf(mn, __shfl_xor(mn, off));
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    const GroupParams gp = group_params(mn, mx, BITS);
+    const int j = c % G;
+    uint32_t bits = code_of_fast(x, gp, (1 << BITS) - 1) << ((j * BITS) % 32);
+#pragma unroll
+    for (int off = CPW / 2; off >= 1; off >>= 1)
+        bits |= __shfl_xor(bits, off);
+    const int ncg = D / G, cg = c / G;
+    const size_t tc = (bh * tcap + n) * ncg + cg;
+    if (j % CPW == 0)
+        codes[tc * (G * BITS / 32) + (j * BITS) / 32] = bits;
+    if (j == 0)
+        meta[tc] = gp.meta;
+}
+
+// Append one token of an operand grouped per channel (one channel over G
+// tokens): thread c writes channel c into tail slot n mod G and, when that
+// slot is the group's last, quantizes the G tail elements of channel c as
+// group n/G.  Every tail element a thread reads was written by the same
+// thread (this launch) or by an earlier launch.
+template <typename T, int BITS>
+__device__ __forceinline__ void append_channel_groups(uint32_t* __restrict__ codes,
+                                                      uint32_t* __restrict__ meta, int gcap,
+                                                      T* __restrict__ tail, T val, size_t bh,
+                                                      int n, int c, int D)
+{
+    constexpr int W = G * BITS / 32;
+    const int slot = n % G;
+    tail[slot * D + c] = val;
+    if (slot != G - 1)
+        return;
+    float x[G];
+#pragma unroll
+    for (int j = 0; j < G - 1; ++j)
+        x[j] = to_f32(tail[j * D + c]);
+    x[G - 1] = to_f32(val);
+    uint32_t w[W];
+    const uint32_t m = quantize_group<BITS>(x, w);
+    const size_t gc = (bh * gcap + n / G) * D + c;
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+        codes[gc * W + i] = w[i];
+    meta[gc] = m;
+}
+
 // Append one token per sequence/head in one launch (block = one sequence/head,
-// head_dim threads, thread c = channel c).
-// Values: the 32 lanes of a channel group find the group's min and max with
-// lane shuffles, each codes its own element, and the codes are OR-reduced
-// into 32-bit words across the lanes that share a word.
-// Keys: thread c writes channel c into tail slot n mod G and, when that slot
-// is the last one, quantizes the full tail as key group n/G; every tail
-// element it reads was written by the same thread (this launch) or by an
-// earlier launch.
+// head_dim threads, thread c = channel c): the value is quantized per token
+// at once, the key goes to the tail and its group is quantized when the tail
+// fills.
 template <typename T, int KBITS, int VBITS>
 __global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __restrict__ v, int n)
 {
-    constexpr int WK = G * KBITS / 32;
-    constexpr int CPW = 32 / VBITS;  // value codes per 32-bit word
     const int D = p.D;
     const int c = threadIdx.x;
     const size_t bh = blockIdx.x;
@@ -139,46 +195,35 @@ __global__ void append_kernel(Planes p, const T* __restrict__ k, const T* __rest
         reinterpret_cast<T*>(p.v_sink)[(bh * p.sink + n) * D + c] = v[bh * D + c];
         return;
     }
-    {
-        const float x = to_f32(v[bh * D + c]);
-        float mn = x, mx = x;
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) {  // within the 32-lane group
-            mn = fminf(mn, __shfl_xor(mn, off));
-            mx = fmaxf(mx, __shfl_xor(mx, off));
-        }
-        const GroupParams gp = group_params(mn, mx, VBITS);
-        const int j = c % G;
-        uint32_t bits = code_of_fast(x, gp, (1 << VBITS) - 1) << ((j * VBITS) % 32);
-#pragma unroll
-        for (int off = CPW / 2; off >= 1; off >>= 1)
-            bits |= __shfl_xor(bits, off);
-        const int ncg = D / G, cg = c / G;
-        const size_t tc = (bh * p.tcap + n) * ncg + cg;
-        if (j % CPW == 0)
-            p.v_codes[tc * (G * VBITS / 32) + (j * VBITS) / 32] = bits;
-        if (j == 0)
-            p.v_meta[tc] = gp.meta;
-    }
-    T* tail = reinterpret_cast<T*>(p.k_tail) + bh * p.ring * D;  // ring of G slots
-    const int slot = n % G;
-    const T val = k[bh * D + c];
-    tail[slot * D + c] = val;
-    if (slot != G - 1)
+    append_token_groups<T, VBITS>(p.v_codes, p.v_meta, p.tcap, v + bh * D, bh, n, c, D);
+    append_channel_groups<T, KBITS>(p.k_codes, p.k_meta, p.gcap,
+                                    reinterpret_cast<T*>(p.k_tail) + bh * p.ring * D,
+                                    k[bh * D + c], bh, n, c, D);
+}
+
+// The same for the geometry ablation (no windows): each operand is appended
+// the way its grouping axis needs.
+template <typename T, int KBITS, int VBITS, int GEOM>
+__global__ void append_geometry_kernel(Planes p, const T* __restrict__ k,
+                                       const T* __restrict__ v, int n)
+{
+    const int D = p.D;
+    const int c = threadIdx.x;
+    const size_t bh = blockIdx.x;
+    if (c >= D)
         return;
-    float x[G];
-#pragma unroll
-    for (int j = 0; j < G - 1; ++j)
-        x[j] = to_f32(tail[j * D + c]);
-    x[G - 1] = to_f32(val);
-    uint32_t w[WK];
-    const uint32_t meta = quantize_group<KBITS>(x, w);
-    const size_t gc = (bh * p.gcap + n / G) * D + c;
-    uint32_t* dst = p.k_codes + gc * WK;
-#pragma unroll
-    for (int i = 0; i < WK; ++i)
-        dst[i] = w[i];
-    p.k_meta[gc] = meta;
+    if (GEOM & kKeysPerToken)
+        append_token_groups<T, KBITS>(p.k_codes, p.k_meta, p.tcap, k + bh * D, bh, n, c, D);
+    else
+        append_channel_groups<T, KBITS>(p.k_codes, p.k_meta, p.gcap,
+                                        reinterpret_cast<T*>(p.k_tail) + bh * p.ring * D,
+                                        k[bh * D + c], bh, n, c, D);
+    if (GEOM & kValuesPerChannel)
+        append_channel_groups<T, VBITS>(p.v_codes, p.v_meta, p.gcap,
+                                        reinterpret_cast<T*>(p.v_tail) + bh * p.ring * D,
+                                        v[bh * D + c], bh, n, c, D);
+    else
+        append_token_groups<T, VBITS>(p.v_codes, p.v_meta, p.tcap, v + bh * D, bh, n, c, D);
 }
 
 // Append with a residual window (R > 0): key and value of token n go to ring
@@ -247,10 +292,82 @@ __global__ void append_residual_kernel(Planes p, const T* __restrict__ k,
 
 // ------------------------------------------------------------- dispatch --
 
+// Channel groups [g_begin, g_end) of src into the planes `codes`/`meta`
+// (laid out [gcap][D][W]) and token groups of n_src tokens into planes laid
+// out [tcap][D/G][W]: the two quantize kernels, pointed at any plane pair.
+template <typename T>
+void quantize_channel_groups(Planes q, uint32_t* codes, uint32_t* meta, int bits, const T* src,
+                             int n_tokens, int g_begin, int g_end, hipStream_t stream)
+{
+    if (g_end <= g_begin)
+        return;
+    q.k_codes = codes;
+    q.k_meta = meta;
+    const int gpb = 256 / q.D;
+    dim3 grid((g_end - g_begin + gpb - 1) / gpb, q.nb * q.hkv);
+    switch (bits) {
+    case 2: quant_keys_kernel<T, 2><<<grid, gpb * q.D, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    case 4: quant_keys_kernel<T, 4><<<grid, gpb * q.D, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    case 8: quant_keys_kernel<T, 8><<<grid, gpb * q.D, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    }
+}
+
+template <typename T>
+void quantize_token_groups(Planes q, uint32_t* codes, uint32_t* meta, int bits, const T* src,
+                           int n_src, int src_stride, int t_dst0, hipStream_t stream)
+{
+    const size_t total = n_src > 0 ? (size_t)q.nb * q.hkv * n_src * (q.D / G) : 0;
+    if (total == 0)
+        return;
+    q.v_codes = codes;
+    q.v_meta = meta;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    switch (bits) {
+    case 2: quant_values_kernel<T, 2><<<blocks, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, total); break;
+    case 4: quant_values_kernel<T, 4><<<blocks, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, total); break;
+    case 8: quant_values_kernel<T, 8><<<blocks, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, total); break;
+    }
+}
+
+template <typename T>
+void copy_rows(const Planes& p, const T* src, void* dst, int slots, int n_tokens, int t0, int t1,
+               hipStream_t stream)
+{
+    const size_t total = t1 > t0 ? (size_t)p.nb * p.hkv * (t1 - t0) * p.D : 0;
+    if (total > 0)
+        copy_tail_kernel<T><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
+            p, src, static_cast<T*>(dst), slots, n_tokens, t0, t1, total);
+}
+
+// Prefill with a non-zero geometry (no windows): an operand grouped per
+// channel gets groups [0, n/G) and its last n mod G tokens in its tail; one
+// grouped per token gets every token.
+template <typename T>
+hipError_t quantize_prefill_geometry(const Planes& p, const T* k, const T* v, int n_tokens,
+                                     hipStream_t stream)
+{
+    const int tq = n_tokens / G * G;
+    if (p.geometry & kKeysPerToken) {
+        quantize_token_groups<T>(p, p.k_codes, p.k_meta, p.kbits, k, n_tokens, n_tokens, 0, stream);
+    } else {
+        quantize_channel_groups<T>(p, p.k_codes, p.k_meta, p.kbits, k, n_tokens, 0, tq / G, stream);
+        copy_rows<T>(p, k, p.k_tail, p.ring, n_tokens, tq, n_tokens, stream);
+    }
+    if (p.geometry & kValuesPerChannel) {
+        quantize_channel_groups<T>(p, p.v_codes, p.v_meta, p.vbits, v, n_tokens, 0, tq / G, stream);
+        copy_rows<T>(p, v, p.v_tail, p.ring, n_tokens, tq, n_tokens, stream);
+    } else {
+        quantize_token_groups<T>(p, p.v_codes, p.v_meta, p.vbits, v, n_tokens, n_tokens, 0, stream);
+    }
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tokens,
                               hipStream_t stream)
 {
+    if (p.geometry != 0)
+        return quantize_prefill_geometry<T>(p, k, v, n_tokens, stream);
     // sink [0, ns), quantized [S, tq), rings [tq, n_tokens)
     const int ns = n_tokens < p.sink ? n_tokens : p.sink;
     const int tq = quantized_end(n_tokens, p.residual, p.sink);
@@ -293,10 +410,29 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
     return hipGetLastError();
 }
 
+template <typename T, int KBITS, int VBITS>
+void append_geometry(const Planes& p, const T* k, const T* v, int n, hipStream_t stream)
+{
+    const int nbh = p.nb * p.hkv;
+    switch (p.geometry) {
+    case 1: append_geometry_kernel<T, KBITS, VBITS, 1><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+    case 2: append_geometry_kernel<T, KBITS, VBITS, 2><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+    case 3: append_geometry_kernel<T, KBITS, VBITS, 3><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;
+    }
+}
+
 template <typename T, int KBITS>
 void append_kb(const Planes& p, const T* k, const T* v, int n, hipStream_t stream)
 {
     const int nbh = p.nb * p.hkv;
+    if (p.geometry != 0) {
+        switch (p.vbits) {
+        case 2: append_geometry<T, KBITS, 2>(p, k, v, n, stream); break;
+        case 4: append_geometry<T, KBITS, 4>(p, k, v, n, stream); break;
+        case 8: append_geometry<T, KBITS, 8>(p, k, v, n, stream); break;
+        }
+        return;
+    }
     if (p.residual > 0) {
         switch (p.vbits) {
         case 2: append_residual_kernel<T, KBITS, 2><<<nbh, p.D, 0, stream>>>(p, k, v, n); break;

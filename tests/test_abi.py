@@ -101,6 +101,8 @@ def test_layout_with_residual_window():
     ("sink", -32, L.KVQ_ERR_ARG),
     ("sink", 40, L.KVQ_ERR_UNSUPPORTED),
     ("sink", 2048, L.KVQ_ERR_UNSUPPORTED),
+    ("geometry", -1, L.KVQ_ERR_ARG),
+    ("geometry", 4, L.KVQ_ERR_ARG),
 ])
 def test_bad_configs_rejected_on_host(field, value, status):
     c = cfg(**{field: value})
@@ -110,6 +112,32 @@ def test_bad_configs_rejected_on_host(field, value, status):
     # create fails the same way before touching the device
     st, h = L.kvq_create(c, 0x10000, 1 << 40)
     assert st == status and h is None
+
+
+@pytest.mark.parametrize("geometry", [1, 2, 3])
+@pytest.mark.parametrize("window", [dict(residual=32), dict(sink=32)])
+def test_geometry_ablation_has_no_windows(geometry, window):
+    c = cfg(geometry=geometry, **window)
+    assert L.kvq_layout_for(c)[0] == L.KVQ_ERR_UNSUPPORTED
+    assert L.kvq_workspace_bytes(cfg(geometry=geometry)) > 0
+
+
+def test_layout_with_values_per_channel():
+    """Flipped planes keep their sizes; values grouped per channel get a
+    G-slot tail (keys per token leave the key tail unused)."""
+    _, lay0 = L.kvq_layout_for(cfg())
+    for geometry in (1, 2, 3):
+        st, lay = L.kvq_layout_for(cfg(geometry=geometry))
+        assert st == L.KVQ_OK and lay.tail_slots == 32
+        assert (lay.k_meta - lay.k_codes, lay.v_codes - lay.k_meta, lay.v_meta - lay.v_codes,
+                lay.k_tail - lay.v_meta) == (lay0.k_meta - lay0.k_codes,
+                                             lay0.v_codes - lay0.k_meta,
+                                             lay0.v_meta - lay0.v_codes,
+                                             lay0.k_tail - lay0.v_meta)
+        if geometry & L.KVQ_VALUES_PER_CHANNEL:
+            assert lay.k_sink - lay.v_tail >= 2 * 2 * 32 * 128 * 2
+        else:
+            assert lay.k_sink == lay.v_tail
 
 
 def test_create_rejects_bad_workspace_before_any_hip_call():
@@ -128,6 +156,7 @@ def test_null_handle_calls():
     assert L.kvq_quantize_prefill(None, 1, 1, 4, None) == L.KVQ_ERR_ARG
     assert L.kvq_append_token(None, 1, 1, None) == L.KVQ_ERR_ARG
     assert L.kvq_attend_decode(None, 1, 1, None) == L.KVQ_ERR_ARG
+    assert L.kvq_error_metrics(None, 1, 1, 1, 1, None) == L.KVQ_ERR_ARG
 
 
 def test_strerror_covers_every_status():
