@@ -80,6 +80,14 @@ def lib() -> ctypes.CDLL:
         L.orc_error_metrics.argtypes = [i, i, i, i, i, i, i, i, i, i, i, i, d, P, P, P,
                                         P, P, P, P, P, i, P, P, P, i, i, i, P]
         L.orc_error_metrics.restype = i
+        L.orc_fp8_decode.argtypes = [ctypes.c_uint8]
+        L.orc_fp8_decode.restype = d
+        L.orc_fp8_encode.argtypes = [d]
+        L.orc_fp8_encode.restype = ctypes.c_uint8
+        L.orc_quantize_fp8.argtypes = [P, i, i, i, i, i, i, i, P]
+        L.orc_quantize_fp8.restype = i
+        L.orc_attend_fp8.argtypes = [i, i, i, i, i, i, d, P, P, i, P, i, i, i, P]
+        L.orc_attend_fp8.restype = i
         _lib = L
     return _lib
 
@@ -386,3 +394,41 @@ def error_metrics(planes: dict, k: np.ndarray, v: np.ndarray, q: np.ndarray, n: 
     if rc != 0:
         raise ValueError("orc_error_metrics failed")
     return summarize_metrics(out), out
+
+
+# ------------------------------------------------------------ FP8 E4M3 cache
+
+def fp8_decode(b: int) -> float:
+    return lib().orc_fp8_decode(int(b))
+
+
+def fp8_encode(x: float) -> int:
+    return lib().orc_fp8_encode(float(x))
+
+
+def quantize_fp8(x: np.ndarray, G: int = 32, max_tokens=None) -> np.ndarray:
+    """FP8 E4M3 planes uint8[nb][Hkv][Gcap][D][G] of x[nb][Hkv][T][D]."""
+    x = np.ascontiguousarray(x)
+    nb, hkv, T, D = x.shape
+    cap = T if max_tokens is None else max_tokens
+    gcap = -(-max(cap, 1) // G)
+    out = np.zeros((nb, hkv, gcap, D, G), dtype=np.uint8)
+    if lib().orc_quantize_fp8(_ptr(x), _dtype_code(x), nb, hkv, T, D, G, gcap, _ptr(out)) != 0:
+        raise ValueError("orc_quantize_fp8 failed")
+    return out
+
+
+def attend_fp8(k8: np.ndarray, v8: np.ndarray, q: np.ndarray, n: int, hkv: int, G: int = 32,
+               base: float = 10000.0, rows=None) -> np.ndarray:
+    """Decode attention over FP8 planes (``quantize_fp8``) for q[nb][Hq][D]."""
+    q = np.ascontiguousarray(q)
+    nb, hq, D = q.shape
+    k8 = np.ascontiguousarray(k8, dtype=np.uint8)
+    v8 = np.ascontiguousarray(v8, dtype=np.uint8)
+    r0, r1 = (0, nb * hq) if rows is None else rows
+    out = np.zeros((r1 - r0, D), dtype=np.float64)
+    rc = lib().orc_attend_fp8(nb, hq, hkv, D, G, k8.shape[2], float(base), _ptr(k8), _ptr(v8),
+                              _dtype_code(q), _ptr(q), n, r0, r1, _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_attend_fp8 failed")
+    return out.reshape(nb, hq, D) if rows is None else out

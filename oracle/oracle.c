@@ -51,6 +51,14 @@
  *   5. Attention output = softmax-weighted sum of the value vectors over all
  *      cached tokens, scores scaled by 1/sqrt(D).  [BITS, "Values: Where the
  *      Intuition Breaks"].  Softmax is the plain two-pass form.
+ *   7. FP8 cache ([ROT], "Key Takeaways" and the practical guidance: FP8 is
+ *      the production default at 2x capacity): every key and value element
+ *      stored as one OCP FP8 E4M3 byte (1 sign, 4 exponent bits with bias 7,
+ *      3 mantissa bits; largest finite 448; no infinities).  Readings: no
+ *      scale factor (scale 1); round to nearest, ties to even, values beyond
+ *      the largest finite saturate to +-448; keys stored before the rotary
+ *      embedding like the integer cache; bytes channel-major inside 32-token
+ *      groups, [nb][Hkv][Gcap][D][32], the integer key layout at 8 bits.
  *   6. Geometry ablation ([BITS], lede and "Keys: The Outliers Live in Fixed
  *      Channels", "Values: Where the Intuition Breaks"): the same 2 bits
  *      spent along the other axis -- keys per token (a group is G channels
@@ -729,5 +737,115 @@ int orc_error_metrics(int nb, int hq, int hkv, int D, int G, int kbits,
         }
     }
     free(a); free(ah); free(kx); free(kh); free(vx); free(vh); free(qr); free(o);
+    return 0;
+}
+
+/* ------------------------------------------------------------- FP8 E4M3 */
+
+/* Value of an OCP FP8 E4M3 byte: sign, exponent e (bias 7), mantissa m:
+ * e = 0 is subnormal, m * 2^-9; e = 15 with m = 7 is NaN. */
+double orc_fp8_decode(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Nearest E4M3 byte to x (finite), ties to the even mantissa, magnitudes at
+ * or above 448 saturate to 448. */
+uint8_t orc_fp8_encode(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int e2;
+    frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;         /* a in [2^e, 2^(e+1)) */
+    if (e < -6)
+        e = -6;             /* subnormal steps are 2^-9 like the lowest binade */
+    double q = rint(ldexp(a, 3 - e));   /* multiples of 2^(e-3), ties to even */
+    if (a < ldexp(1.0, -6)) {           /* subnormal: code = q (q = 8 is 2^-6) */
+        return sign | (uint8_t)q;
+    }
+    if (q >= 16.0) {        /* rounded up into the next binade */
+        q = 8.0;
+        e += 1;
+    }
+    return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
+}
+
+/* FP8 planes for T tokens of x[nb][Hkv][T][D] (keys or values): byte j of
+ * row (g, c) holds token gG + j, channel c; bytes of a partly filled group
+ * past T are 0. */
+int orc_quantize_fp8(const void* x, int dtype, int nb, int hkv, int T, int D,
+                     int G, int gcap, uint8_t* planes)
+{
+    if (G <= 0 || T < 0 || (T + G - 1) / G > gcap)
+        return -1;
+    int ng = (T + G - 1) / G;
+    for (int b = 0; b < nb; ++b)
+        for (int h = 0; h < hkv; ++h) {
+            size_t bh = (size_t)b * hkv + h;
+            for (int g = 0; g < ng; ++g)
+                for (int c = 0; c < D; ++c)
+                    for (int j = 0; j < G; ++j) {
+                        int t = g * G + j;
+                        size_t o = ((bh * gcap + g) * D + c) * G + j;
+                        planes[o] = t < T ? orc_fp8_encode(load_elem(
+                                                x, dtype, (bh * T + t) * D + c))
+                                          : 0;
+                    }
+        }
+    return 0;
+}
+
+/* Decode attention over FP8 planes (the layout above) for rows
+ * [row_begin, row_end): keys decoded and rotated to position t, the query
+ * to n-1, scores / sqrt(D), softmax-weighted sum of the decoded values. */
+int orc_attend_fp8(int nb, int hq, int hkv, int D, int G, int gcap, double base,
+                   const uint8_t* k8, const uint8_t* v8, int dtype,
+                   const void* q, int n, int row_begin, int row_end,
+                   double* out)
+{
+    if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 ||
+        (n + G - 1) / G > gcap || row_begin < 0 || row_end > nb * hq)
+        return -1;
+    double* score = (double*)malloc(sizeof(double) * (size_t)n);
+    double* vals = (double*)malloc(sizeof(double) * (size_t)n * D);
+    double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!score || !vals || !qr || !kr) {
+        free(score); free(vals); free(qr); free(kr);
+        return -2;
+    }
+    int group = hq / hkv;
+    for (int r = row_begin; r < row_end; ++r) {
+        int b = r / hq, h = r % hq, kvh = h / group;
+        size_t bh = (size_t)b * hkv + kvh;
+        for (int c = 0; c < D; ++c)
+            qr[c] = load_elem(q, dtype, (size_t)r * D + c);
+        orc_rope(qr, D, (double)(n - 1), base);
+        for (int t = 0; t < n; ++t) {
+            for (int c = 0; c < D; ++c) {
+                size_t o = ((bh * gcap + t / G) * D + c) * G + t % G;
+                kr[c] = orc_fp8_decode(k8[o]);
+                vals[(size_t)t * D + c] = orc_fp8_decode(v8[o]);
+            }
+            orc_rope(kr, D, (double)t, base);
+            double dot = 0.0;
+            for (int c = 0; c < D; ++c)
+                dot += qr[c] * kr[c];
+            score[t] = dot / sqrt((double)D);
+        }
+        softmax_sum(score, vals, n, D, out + (size_t)(r - row_begin) * D);
+    }
+    free(score); free(vals); free(qr); free(kr);
     return 0;
 }
