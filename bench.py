@@ -125,6 +125,15 @@ def attend_flops(cfg, n: int) -> int:
     return cfg.batch * cfg.kv_heads * n * cfg.head_dim * (7 + 4 * qpk)
 
 
+def fp8_bytes(cfg, n: int, with_q: bool = True) -> int:
+    """One E4M3 byte per cached key and value element (+ q and out); the
+    prefill moves 2 input bytes in and 1 out per element (3x the cache at
+    fp16 inputs, reported as 3 * fp8_bytes without q)."""
+    esz = 2 if cfg.dtype == "float16" else 4
+    kv = 2 * cfg.batch * cfg.kv_heads * n * cfg.head_dim
+    return kv + (cfg.batch * cfg.q_heads * cfg.head_dim * (esz + 4) if with_q else 0)
+
+
 def prefill_bytes(cfg, n: int, residual: int = 0, sink: int = 0, geometry: int = 0) -> int:
     """Quantize-and-pack of n tokens: K and V read once, planes written."""
     esz = 2 if cfg.dtype == "float16" else 4
@@ -171,7 +180,7 @@ class HipEvents:
 
 
 def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0, sink: int = 0,
-                 geometry: int = 0):
+                 geometry: int = 0, fp8: bool = False):
     """The oracle (plain single-threaded fp64 C) on a bounded sample of the
     same workload: decode attention for whole sequences, rows timed until
     about budget_s seconds of CPU work."""
@@ -186,11 +195,14 @@ def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0, sink: i
     q = synth.make_query(cfg, 0, 0)
     rows_done, t_total, bytes_done = 0, 0.0, 0
     one = synth.scaled(cfg, batch=1)
-    per_row = attend_bytes(one, n, residual, sink, geometry) / cfg.q_heads
+    per_row = (fp8_bytes(one, n) if fp8 else attend_bytes(one, n, residual, sink, geometry)) \
+        / cfg.q_heads
     for b in range(cfg.batch):
         k = synth.make_keys(cfg, 0, 0, n, seqs=[b])
         v = synth.make_values(cfg, 0, 0, n, seqs=[b])
-        if geometry:
+        if fp8:
+            pl = (oracle.quantize_fp8(k, cfg.group), oracle.quantize_fp8(v, cfg.group))
+        elif geometry:
             pl = oracle.geometry_planes(k, v, cfg.key_bits, cfg.value_bits, geometry, cfg.group)
         else:
             kp = oracle.quantize_keys(k, cfg.key_bits, cfg.group, residual=residual, sink=sink)
@@ -204,7 +216,10 @@ def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0, sink: i
                 pl["k_sink"], pl["v_sink"] = kp[3], vals[-1]
         for r in range(cfg.q_heads):
             t0 = time.perf_counter()
-            if geometry:
+            if fp8:
+                oracle.attend_fp8(pl[0], pl[1], q[b:b + 1], n, cfg.kv_heads, cfg.group,
+                                  cfg.rope_base, rows=(r, r + 1))
+            elif geometry:
                 oracle.attend_geometry(pl, q[b:b + 1], n, cfg.key_bits, cfg.value_bits,
                                        cfg.kv_heads, geometry, cfg.group, cfg.rope_base,
                                        rows=(r, r + 1))
@@ -245,6 +260,8 @@ def main():
                     help="first tokens kept in full precision (a multiple of 32)")
     ap.add_argument("--geometry", default="kivi", choices=sorted(GEOMETRIES),
                     help="grouping axes (the ablation flips keys and/or values; no windows)")
+    ap.add_argument("--format", default="int", choices=["int", "fp8"],
+                    help="fp8: E4M3 bytes for keys and values (8 bits each, no windows)")
     ap.add_argument("--no-metrics", action="store_true",
                     help="skip the error-where-consumed metrics of the prompt cache")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -270,13 +287,17 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cfg = synth.CONFIGS[args.config]
+    fp8 = args.format == "fp8"
+    if fp8:
+        cfg = synth.scaled(cfg, key_bits=8, value_bits=8,
+                           description=cfg.description + "; FP8 E4M3 keys and values")
     n = cfg.n_tokens
     tdt = torch.float16 if cfg.dtype == "float16" else torch.float32
     total_steps = args.warmup + args.steps
 
     Rw, Sw = args.residual, args.sink
     geom = GEOMETRIES[args.geometry]
-    one_cache = attend_bytes(cfg, n, Rw, Sw, geom)
+    one_cache = fp8_bytes(cfg, n) if fp8 else attend_bytes(cfg, n, Rw, Sw, geom)
     R = args.caches or max(2, math.ceil(2 * INFINITY_CACHE / one_cache) + 1)
     visits = math.ceil(total_steps / R)
     max_tokens = n + visits
@@ -293,7 +314,7 @@ def main():
 
     caches = [QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
                                cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev,
-                               residual=Rw, sink=Sw, geometry=geom)
+                               residual=Rw, sink=Sw, geometry=geom, format=int(fp8))
               for _ in range(R)]
     # prefill (quantize-and-pack of the whole prompt), timed per cache after
     # one untimed prefill of a one-group cache (first launches load the code)
@@ -313,7 +334,7 @@ def main():
     # error where it is consumed, on the first cache's prompt (before the
     # appends): the unquantized prompt keys and values are still at hand
     metrics = None
-    if not args.no_metrics:
+    if not args.no_metrics and not fp8:
         q_prompt = torch.from_numpy(synth.make_query(cfg, 0, 0)).to(dev)
         mv = caches[0].error_metrics(k, v, q_prompt).cpu().numpy()
         metrics = {name: float(x) for name, x in zip(
@@ -369,7 +390,8 @@ def main():
         raise RuntimeError("cache lengths do not match the steps issued")
 
     wall = t1 - t0
-    total_bytes = sum(attend_bytes(cfg, L, Rw, Sw, geom) for L in lengths)
+    total_bytes = sum((fp8_bytes(cfg, L) if fp8 else attend_bytes(cfg, L, Rw, Sw, geom))
+                      for L in lengths)
     value = total_bytes / wall / 1e9
     attend_ms = np.array([hev.elapsed_ms(2 * j, 2 * j + 1) for j in range(args.steps)])
     hev.close()
@@ -400,6 +422,7 @@ def main():
             "residual": Rw,
             "sink": Sw,
             "geometry": args.geometry,
+            "format": "fp8_e4m3" if fp8 else "int",
             "context_during_steps": [min(lengths), max(lengths)],
             "rotating_caches": R,
             "parallelism": "single GPU",
@@ -413,8 +436,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
             "traffic": (measured_traffic(cfg.name) if Rw == 0 and Sw == 0 and geom == 0
-                        else None),
-            "kernel": ("attend_kernel (decode attention)" if geom == 0 else
+                        and not fp8 else None),
+            "kernel": ("attend_fp8_kernel (FP8 E4M3 decode attention)" if fp8 else
+                       "attend_kernel (decode attention)" if geom == 0 else
                        "attend_geometry_kernel (geometry ablation attention)")
                       + "; HIP events around each kvq_attend_decode call in the timed loop",
             "flops_per_launch": int(flops_per_launch),
@@ -428,7 +452,8 @@ def main():
         "prefill": {
             "tokens": n - 1,
             "median_ms": round(float(np.median(pf_ms)), 4),
-            "GB_per_s": round(prefill_bytes(cfg, n - 1, Rw, Sw, geom)
+            "GB_per_s": round((3 * fp8_bytes(cfg, n - 1, with_q=False) if fp8 else
+                               prefill_bytes(cfg, n - 1, Rw, Sw, geom))
                               / (np.median(pf_ms) / 1e3) / 1e9, 2),
             "tokens_per_s": round(cfg.batch * (n - 1) / (np.median(pf_ms) / 1e3), 1),
         },
@@ -438,7 +463,7 @@ def main():
     for c in caches:
         c.close()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, n, residual=Rw, sink=Sw, geometry=geom)
+        res["cpu_baseline"] = cpu_baseline(cfg, n, residual=Rw, sink=Sw, geometry=geom, fp8=fp8)
     print(json.dumps(res), flush=True)
 
 

@@ -86,6 +86,18 @@
  * wait verbatim in V_TAIL (G slots, token t in slot t mod G) until their
  * group fills.  Plane sizes do not change.  A non-zero geometry requires
  * residual == sink == 0; its attention runs in a separate, plain kernel.
+ * FP8 cache, kvq_config.format == KVQ_FORMAT_FP8_E4M3 (the page "Rotate,
+ * Then Round: The Geometry of KV-Cache Compression", key takeaways: FP8 as
+ * the production default): every key and value element is one OCP FP8 E4M3
+ * byte (bias 7, largest finite 448, no infinities), rounded to nearest with
+ * ties to even and saturated at +-448, no scale factor; keys before the
+ * rotary embedding.  K_CODES and V_CODES (sized for 8-bit codes) hold one
+ * head_dim * 32-byte block per (sequence, KV head, 32-token group g),
+ * u8[batch][kv_heads][Gcap][head_dim * 32], in 16-byte pieces: channel c of
+ * token gG + j at byte ((2 (c % 2) + j / 16) (head_dim / 2) + c / 2) * 16
+ * + j % 16 of the block; bytes of the last group past n are 0; K_META,
+ * V_META and the tails are unused.  Its
+ * attention runs in a separate kernel; kvq_error_metrics does not take it.
  * The step and zero are each rounded once, to nearest-even, from the exact
  * value (range/(2^B-1) and the minimum); the code of x is the integer nearest
  * to (x - zero)/step computed exactly, ties to even, clamped to
@@ -120,6 +132,9 @@ enum {
 
 enum { KVQ_F16 = 0, KVQ_F32 = 1 };
 
+/* kvq_config.format: integer codes (the method above) or FP8 E4M3 bytes. */
+enum { KVQ_FORMAT_INT = 0, KVQ_FORMAT_FP8_E4M3 = 1 };
+
 /* kvq_config.geometry bits (0 = keys per channel, values per token). */
 enum { KVQ_KEYS_PER_TOKEN = 1, KVQ_VALUES_PER_CHANNEL = 2 };
 
@@ -150,6 +165,9 @@ typedef struct kvq_config {
                            multiple of group in [0, 1024]; 0 = none         */
     int32_t geometry;   /* 0, or KVQ_KEYS_PER_TOKEN | KVQ_VALUES_PER_CHANNEL
                            (ablation; needs residual == sink == 0)          */
+    int32_t format;     /* KVQ_FORMAT_INT (0) or KVQ_FORMAT_FP8_E4M3 (needs
+                           key_bits == value_bits == 8, no windows,
+                           geometry 0)                                      */
 } kvq_config;
 
 typedef struct kvq_layout {
@@ -239,7 +257,8 @@ int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream);
  *   OUTPUT_REL_ERROR        |sum_t ahat_t vhat_t - sum_t a_t v_t| / |sum_t a_t v_t|.
  * Uses the workspace's partials region as scratch (like kvq_attend_decode:
  * not concurrently with another attend or metrics call on the handle).
- * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (n == 0), KVQ_ERR_HIP. */
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (n == 0), KVQ_ERR_UNSUPPORTED (an FP8
+ * cache), KVQ_ERR_HIP. */
 int kvq_error_metrics(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
                       double* d_metrics, void* stream);
 

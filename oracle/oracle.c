@@ -57,8 +57,12 @@
  *      3 mantissa bits; largest finite 448; no infinities).  Readings: no
  *      scale factor (scale 1); round to nearest, ties to even, values beyond
  *      the largest finite saturate to +-448; keys stored before the rotary
- *      embedding like the integer cache; bytes channel-major inside 32-token
- *      groups, [nb][Hkv][Gcap][D][32], the integer key layout at 8 bits.
+ *      embedding like the integer cache; inside each 32-token group the
+ *      bytes of channel c, token j sit at
+ *        ((2 * (c % 2) + j / 16) * (D / 2) + c / 2) * 16 + j % 16
+ *      of a D * 32-byte block ([nb][Hkv][Gcap][D * 32]): 16-byte pieces, so
+ *      the reader that owns channel pair c/2 finds its four pieces at a
+ *      stride of D * 8 bytes.
  *   6. Geometry ablation ([BITS], lede and "Keys: The Outliers Live in Fixed
  *      Channels", "Values: Where the Intuition Breaks"): the same 2 bits
  *      spent along the other axis -- keys per token (a group is G channels
@@ -781,13 +785,19 @@ uint8_t orc_fp8_encode(double x)
     return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
 }
 
-/* FP8 planes for T tokens of x[nb][Hkv][T][D] (keys or values): byte j of
- * row (g, c) holds token gG + j, channel c; bytes of a partly filled group
- * past T are 0. */
+/* Byte of token j (< 32), channel c inside a group block of D * 32 bytes. */
+static size_t fp8_offset(int D, int c, int j)
+{
+    return ((size_t)(2 * (c % 2) + j / 16) * (D / 2) + c / 2) * 16 + j % 16;
+}
+
+/* FP8 planes for T tokens of x[nb][Hkv][T][D] (keys or values), group g of
+ * sequence/head bh in block bh * gcap + g (G must be 32); bytes of a partly
+ * filled group past T are 0. */
 int orc_quantize_fp8(const void* x, int dtype, int nb, int hkv, int T, int D,
                      int G, int gcap, uint8_t* planes)
 {
-    if (G <= 0 || T < 0 || (T + G - 1) / G > gcap)
+    if (G != 32 || T < 0 || (T + G - 1) / G > gcap || D % 2 != 0)
         return -1;
     int ng = (T + G - 1) / G;
     for (int b = 0; b < nb; ++b)
@@ -797,7 +807,7 @@ int orc_quantize_fp8(const void* x, int dtype, int nb, int hkv, int T, int D,
                 for (int c = 0; c < D; ++c)
                     for (int j = 0; j < G; ++j) {
                         int t = g * G + j;
-                        size_t o = ((bh * gcap + g) * D + c) * G + j;
+                        size_t o = (bh * gcap + g) * D * G + fp8_offset(D, c, j);
                         planes[o] = t < T ? orc_fp8_encode(load_elem(
                                                 x, dtype, (bh * T + t) * D + c))
                                           : 0;
@@ -814,7 +824,7 @@ int orc_attend_fp8(int nb, int hq, int hkv, int D, int G, int gcap, double base,
                    const void* q, int n, int row_begin, int row_end,
                    double* out)
 {
-    if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 ||
+    if (n <= 0 || hkv <= 0 || hq % hkv != 0 || D % 2 != 0 || G != 32 ||
         (n + G - 1) / G > gcap || row_begin < 0 || row_end > nb * hq)
         return -1;
     double* score = (double*)malloc(sizeof(double) * (size_t)n);
@@ -834,7 +844,7 @@ int orc_attend_fp8(int nb, int hq, int hkv, int D, int G, int gcap, double base,
         orc_rope(qr, D, (double)(n - 1), base);
         for (int t = 0; t < n; ++t) {
             for (int c = 0; c < D; ++c) {
-                size_t o = ((bh * gcap + t / G) * D + c) * G + t % G;
+                size_t o = (bh * gcap + t / G) * D * G + fp8_offset(D, c, t % G);
                 kr[c] = orc_fp8_decode(k8[o]);
                 vals[(size_t)t * D + c] = orc_fp8_decode(v8[o]);
             }

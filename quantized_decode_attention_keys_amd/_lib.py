@@ -20,6 +20,9 @@ KVQ_ERR_HIP = -6
 KVQ_F16 = 0
 KVQ_F32 = 1
 
+KVQ_FORMAT_INT = 0
+KVQ_FORMAT_FP8_E4M3 = 1
+
 KVQ_KEYS_PER_TOKEN = 1
 KVQ_VALUES_PER_CHANNEL = 2
 
@@ -59,6 +62,7 @@ class KvqConfig(ctypes.Structure):
         ("residual", ctypes.c_int32),
         ("sink", ctypes.c_int32),
         ("geometry", ctypes.c_int32),
+        ("format", ctypes.c_int32),
     ]
 
 

@@ -25,17 +25,19 @@ class QuantizedKVCache:
     (at least `residual`, fewer than `residual` + group) in full precision,
     `sink` the first `sink` tokens.  `geometry` (ablation, no windows) flips
     the grouping axis: KVQ_KEYS_PER_TOKEN and/or KVQ_VALUES_PER_CHANNEL.
+    `format` KVQ_FORMAT_FP8_E4M3 stores E4M3 bytes instead (key_bits and
+    value_bits 8).
     Calls enqueue on the current torch stream (or `stream`) and return at
     once."""
 
     def __init__(self, batch, q_heads, kv_heads, head_dim, max_tokens, key_bits=2,
                  value_bits=2, dtype=torch.float16, rope_base=10000.0, group=32,
-                 device=None, residual=0, sink=0, geometry=0):
+                 device=None, residual=0, sink=0, geometry=0, format=L.KVQ_FORMAT_INT):
         if dtype not in _DTYPES:
             raise TypeError("dtype must be torch.float16 or torch.float32")
         self.cfg = L.KvqConfig(batch, q_heads, kv_heads, head_dim, max_tokens, group,
                                key_bits, value_bits, _DTYPES[dtype], rope_base, residual,
-                               sink, geometry)
+                               sink, geometry, format)
         self.dtype = dtype
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
             else torch.device(device)
@@ -130,6 +132,12 @@ class QuantizedKVCache:
         by_channel = lambda w: (nb, h, lay.gcap, D, w)  # noqa: E731
         kpt = bool(c.geometry & L.KVQ_KEYS_PER_TOKEN)
         vpc = bool(c.geometry & L.KVQ_VALUES_PER_CHANNEL)
+        if c.format == L.KVQ_FORMAT_FP8_E4M3:
+            # E4M3 bytes of group g, channel c, token j at
+            # [g][c % 2][j // 16][c // 2][j % 16] in both code planes
+            shape = (nb, h, lay.gcap, 2, 2, D // 2, 16)
+            return {"k_fp8": view(lay.k_codes, shape, torch.uint8),
+                    "v_fp8": view(lay.v_codes, shape, torch.uint8)}
         ks = by_token(wk) if kpt else by_channel(wk)
         vs = by_channel(wv) if vpc else by_token(wv)
         return {

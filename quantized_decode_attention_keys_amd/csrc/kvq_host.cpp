@@ -36,7 +36,8 @@ int check_config(const kvq_config* c)
         c->max_tokens < 1 || c->group < 1 || c->key_bits < 1 || c->value_bits < 1 ||
         !(c->rope_base > 1.0f) || !std::isfinite(c->rope_base) || c->q_heads % c->kv_heads != 0 ||
         (c->dtype != KVQ_F16 && c->dtype != KVQ_F32) || c->residual < 0 || c->sink < 0 ||
-        c->geometry < 0 || c->geometry > (KVQ_KEYS_PER_TOKEN | KVQ_VALUES_PER_CHANNEL))
+        c->geometry < 0 || c->geometry > (KVQ_KEYS_PER_TOKEN | KVQ_VALUES_PER_CHANNEL) ||
+        (c->format != KVQ_FORMAT_INT && c->format != KVQ_FORMAT_FP8_E4M3))
         return KVQ_ERR_ARG;
     const int qpk = c->q_heads / c->kv_heads;
     if (c->group != kvqi::kGroup || (c->head_dim != 64 && c->head_dim != 128) ||
@@ -44,12 +45,17 @@ int check_config(const kvq_config* c)
         (c->value_bits != 2 && c->value_bits != 4 && c->value_bits != 8) ||
         (qpk != 1 && qpk != 2 && qpk != 4 && qpk != 8) || c->residual % kvqi::kGroup != 0 ||
         c->residual > kMaxResidual || c->sink % kvqi::kGroup != 0 || c->sink > kMaxResidual ||
-        (c->geometry != 0 && (c->residual != 0 || c->sink != 0)))
+        (c->geometry != 0 && (c->residual != 0 || c->sink != 0)) ||
+        (c->format == KVQ_FORMAT_FP8_E4M3 &&
+         (c->key_bits != 8 || c->value_bits != 8 || c->residual != 0 || c->sink != 0 ||
+          c->geometry != 0)))
         return KVQ_ERR_UNSUPPORTED;
     // keep every plane index inside 2^31 elements per (sequence, head) and
     // the grid dimensions inside their limits
     if ((long long)c->max_tokens > (1LL << 24) || (long long)c->batch * c->q_heads > (1LL << 24) ||
-        (long long)c->batch * c->kv_heads * (qpk / kvqi::block_heads(qpk)) > 65535)
+        (long long)c->batch * c->kv_heads * (qpk / kvqi::block_heads(qpk)) > 65535 ||
+        ((c->geometry != 0 || c->format != KVQ_FORMAT_INT) &&
+         (long long)c->batch * c->q_heads > 65535))  // one block row per output row
         return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
 }
@@ -117,6 +123,7 @@ kvqi::Planes planes_of(const kvq* h)
     p.sink = h->cfg.sink;
     p.geometry = h->cfg.geometry;
     p.rope_base = h->cfg.rope_base;
+    p.format = h->cfg.format;
     return p;
 }
 
@@ -273,8 +280,11 @@ int kvq_quantize_prefill(kvq_t* h, const void* d_k, const void* d_v, int32_t n_t
         return KVQ_ERR_CAPACITY;
     if (n_tokens == 0)
         return KVQ_OK;
-    const int st = hip_status(kvqi::launch_quantize_prefill(
-        planes_of(h), d_k, d_v, n_tokens, static_cast<hipStream_t>(stream)));
+    const kvqi::Planes p = planes_of(h);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int st = hip_status(p.format == kvqi::kFormatFp8
+                                  ? kvqi::launch_fp8_prefill(p, d_k, d_v, n_tokens, s)
+                                  : kvqi::launch_quantize_prefill(p, d_k, d_v, n_tokens, s));
     if (st == KVQ_OK)
         h->n = n_tokens;
     return st;
@@ -286,8 +296,11 @@ int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v, void* stream)
         return KVQ_ERR_ARG;
     if (h->n >= h->cfg.max_tokens)
         return KVQ_ERR_CAPACITY;
-    const int st = hip_status(
-        kvqi::launch_append(planes_of(h), d_k, d_v, h->n, static_cast<hipStream_t>(stream)));
+    const kvqi::Planes p = planes_of(h);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int st = hip_status(p.format == kvqi::kFormatFp8
+                                  ? kvqi::launch_fp8_append(p, d_k, d_v, h->n, s)
+                                  : kvqi::launch_append(p, d_k, d_v, h->n, s));
     if (st == KVQ_OK)
         h->n += 1;
     return st;
@@ -302,15 +315,18 @@ int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream)
     const int n = h->n;
     const kvqi::Planes p = planes_of(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (h->cfg.geometry != 0) {
+    if (h->cfg.geometry != 0 || h->cfg.format != KVQ_FORMAT_INT) {
         // about kTargetBlocks blocks, at least one 32-token chunk per split
         const int rows = h->cfg.batch * h->cfg.q_heads;
         const int chunks = (n + h->cfg.group - 1) / h->cfg.group;
         int splits = (kTargetBlocks + rows - 1) / rows;
+        if (h->force_splits > 0) splits = h->force_splits;
         if (splits > chunks) splits = chunks;
         if (splits > h->layout.max_splits) splits = h->layout.max_splits;
         if (splits < 1) splits = 1;
-        return hip_status(kvqi::launch_attend_geometry(p, d_q, d_out, n, splits, s));
+        return hip_status(h->cfg.format == KVQ_FORMAT_FP8_E4M3
+                              ? kvqi::launch_attend_fp8(p, d_q, d_out, n, splits, s)
+                              : kvqi::launch_attend_geometry(p, d_q, d_out, n, splits, s));
     }
     int splits, waves;
     attend_shape(h, n, &splits, &waves);
@@ -326,6 +342,8 @@ int kvq_error_metrics(kvq_t* h, const void* d_k, const void* d_v, const void* d_
         return KVQ_ERR_ARG;
     if (h->n == 0)
         return KVQ_ERR_STATE;
+    if (h->cfg.format != KVQ_FORMAT_INT)
+        return KVQ_ERR_UNSUPPORTED;
     return hip_status(kvqi::launch_error_metrics(planes_of(h), d_k, d_v, d_q, d_metrics, h->n,
                                                  static_cast<hipStream_t>(stream)));
 }

@@ -36,7 +36,12 @@ struct Planes {
     int sink;            // S
     int geometry;        // 0, or kKeysPerToken | kValuesPerChannel (then R = S = 0)
     double rope_base;    // theta_i = rope_base^(-2i/D) (fp64 paths recompute angles)
+    int format;          // 0: integer codes; kFormatFp8: E4M3 bytes in k_codes/v_codes
 };
+
+// FP8 (E4M3) cache: one byte per element, channel-major in 32-token groups,
+// [nb][hkv][gcap][D][32] inside the k_codes and v_codes planes.
+constexpr int kFormatFp8 = 1;
 
 // Geometry ablation bits: keys grouped like values (G channels of one token,
 // planes [tcap][D/G][wk]) and values grouped like keys (one channel over G
@@ -75,6 +80,13 @@ hipError_t launch_attend_d128(const Planes& p, const void* q, float* out, int n,
 // Attention over a cache with a non-zero geometry (kvq_geometry.hip).
 hipError_t launch_attend_geometry(const Planes& p, const void* q, float* out, int n,
                                   int splits, hipStream_t stream);
+// FP8 cache (kvq_fp8.hip).
+hipError_t launch_fp8_prefill(const Planes& p, const void* k, const void* v, int n,
+                              hipStream_t stream);
+hipError_t launch_fp8_append(const Planes& p, const void* k, const void* v, int n,
+                             hipStream_t stream);
+hipError_t launch_attend_fp8(const Planes& p, const void* q, float* out, int n, int splits,
+                             hipStream_t stream);
 // Error where it is consumed: fp64, any geometry and windows; uses the
 // partials region as scratch for per-row sums (kvq_geometry.hip).
 hipError_t launch_error_metrics(const Planes& p, const void* k, const void* v, const void* q,

@@ -103,6 +103,8 @@ def test_layout_with_residual_window():
     ("sink", 2048, L.KVQ_ERR_UNSUPPORTED),
     ("geometry", -1, L.KVQ_ERR_ARG),
     ("geometry", 4, L.KVQ_ERR_ARG),
+    ("format", 2, L.KVQ_ERR_ARG),
+    ("format", 1, L.KVQ_ERR_UNSUPPORTED),         # FP8 needs key_bits == value_bits == 8
 ])
 def test_bad_configs_rejected_on_host(field, value, status):
     c = cfg(**{field: value})
@@ -120,6 +122,16 @@ def test_geometry_ablation_has_no_windows(geometry, window):
     c = cfg(geometry=geometry, **window)
     assert L.kvq_layout_for(c)[0] == L.KVQ_ERR_UNSUPPORTED
     assert L.kvq_workspace_bytes(cfg(geometry=geometry)) > 0
+
+
+@pytest.mark.parametrize("extra", [dict(residual=32), dict(sink=32), dict(geometry=1),
+                                   dict(batch=1100, q_heads=64, kv_heads=8)])
+def test_fp8_limits(extra):
+    c = cfg(key_bits=8, value_bits=8, format=L.KVQ_FORMAT_FP8_E4M3, **extra)
+    assert L.kvq_layout_for(c)[0] == L.KVQ_ERR_UNSUPPORTED
+    st, lay = L.kvq_layout_for(cfg(key_bits=8, value_bits=8, format=L.KVQ_FORMAT_FP8_E4M3))
+    _, lay8 = L.kvq_layout_for(cfg(key_bits=8, value_bits=8))
+    assert st == L.KVQ_OK and lay.total_bytes == lay8.total_bytes
 
 
 def test_layout_with_values_per_channel():

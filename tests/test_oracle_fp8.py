@@ -1,7 +1,8 @@
 """Pins for the oracle's FP8 (OCP E4M3) cache ("Rotate, Then Round: The
 Geometry of KV-Cache Compression", key takeaways: FP8 as the production
 default).  Readings: round to nearest, ties to even, saturation at +-448,
-no scale factor, bytes channel-major inside 32-token groups.
+no scale factor, bytes of a 32-token group in 16-byte pieces (channel
+parity, token half, channel pair, token mod 16).
 
 The format is checked against its definition (closed-form values of named
 codes, symmetry, ordering), the encoder by brute force over every finite
@@ -88,16 +89,30 @@ def test_round_trip_error_bound(orc):
 
 @pytest.mark.parametrize("T", [1, 31, 32, 77])
 def test_planes_layout(orc, T):
+    """Byte of token t = 32g + j, channel c at offset
+    ((2 (c mod 2) + j div 16) (D/2) + c div 2) 16 + j mod 16 of group block g,
+    checked on the flat bytes."""
     rng = np.random.default_rng(T)
     x = (rng.standard_normal((2, 3, T, D)) * 20).astype(np.float16)
     pl = orc.quantize_fp8(x, max_tokens=96)
-    assert pl.shape == (2, 3, 3, D, G)
+    assert pl.shape == (2, 3, 3, 2, 2, D // 2, 16)
+    flat = pl.reshape(2, 3, 3, D * G)
     table = _table(orc)
+    c = np.arange(D)
+    for t in range(-(-T // G) * G):
+        j = t % G
+        off = ((2 * (c % 2) + j // 16) * (D // 2) + c // 2) * 16 + j % 16
+        got = flat[:, :, t // G][:, :, off]
+        if t < T:
+            want = _brute_encode(x[:, :, t].astype(np.float64).ravel(), table).reshape(2, 3, D)
+            assert np.array_equal(got, want)
+        else:
+            assert not got.any()
+    # the logical view reads the same bytes
+    view = orc.fp8_view(pl)
     for t in range(T):
-        want = _brute_encode(x[:, :, t].astype(np.float64).ravel(), table).reshape(2, 3, D)
-        assert np.array_equal(pl[:, :, t // G, :, t % G], want)
-    for t in range(T, -(-T // G) * G):
-        assert not pl[:, :, t // G, :, t % G].any()
+        assert np.array_equal(view[:, :, t // G, :, t % G], flat[:, :, t // G][
+            :, :, ((2 * (c % 2) + (t % G) // 16) * (D // 2) + c // 2) * 16 + t % 16])
 
 
 @pytest.mark.parametrize("n", [1, 33, 100])
@@ -110,7 +125,8 @@ def test_attention_equals_dense_on_decoded(orc, n):
     k8, v8 = orc.quantize_fp8(k, max_tokens=128), orc.quantize_fp8(v, max_tokens=128)
     out = orc.attend_fp8(k8, v8, q, n, hkv=2)
     dec = np.vectorize(orc.fp8_decode)
-    kd = np.stack([dec(k8[:, :, t // G, :, t % G]) for t in range(n)], axis=2)
-    vd = np.stack([dec(v8[:, :, t // G, :, t % G]) for t in range(n)], axis=2)
+    kv, vv = orc.fp8_view(k8), orc.fp8_view(v8)
+    kd = np.stack([dec(kv[:, :, t // G, :, t % G]) for t in range(n)], axis=2)
+    vd = np.stack([dec(vv[:, :, t // G, :, t % G]) for t in range(n)], axis=2)
     dense = orc.attend_dense(kd.astype(np.float32), vd.astype(np.float32), q.astype(np.float32))
     assert np.allclose(out, dense, rtol=0, atol=1e-12)
