@@ -110,6 +110,16 @@ struct Codec {
 __device__ __forceinline__ float lo_h(uint32_t v) { return __half2float(__ushort_as_half((unsigned short)(v & 0xffffu))); }
 __device__ __forceinline__ float hi_h(uint32_t v) { return __half2float(__ushort_as_half((unsigned short)(v >> 16))); }
 
+// Two binary16 values as one operand of v_dot2_f32_f16.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half2v pack_h2(float lo, float hi)
+{
+    half2v r;
+    r.x = (_Float16)lo;  // nearest-even
+    r.y = (_Float16)hi;
+    return r;
+}
+
 // Value of v in another lane of the same 16-lane row (DPP, VALU only).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
@@ -122,6 +132,19 @@ constexpr int kDppXor2 = 0x4e;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane k <-> 7-k within each 8
 constexpr int kDppMirror = 0x140;     // lane k <-> 15-k within each 16
 constexpr int kDppRor8 = 0x128;       // lane k <- lane (k+8) mod 16 within each 16
+
+// As dpp<CTRL> for patterns that read a lane of the same row for every lane
+// (quad permutations, mirrors), so no old value is needed.
+template <int CTRL>
+__device__ __forceinline__ float dpp_all(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+// max(a, b) for operands that are never NaN: a compare and a select, where
+// fmaxf would first quiet both operands.
+__device__ __forceinline__ float max_nn(float a, float b) { return a > b ? a : b; }
 
 // Cross-row exchanges on the VALU (no LDS round trip).  With both operands
 // equal to v, the 16-lane swap returns {rows (0,0,2,2) of v, rows (1,1,3,3)}
@@ -153,15 +176,15 @@ __device__ __forceinline__ float half_sum(float v)
 template <bool HALVES_EQUAL>
 __device__ __forceinline__ float wave_max(float v)
 {
-    v = fmaxf(v, dpp<kDppXor1>(v));
-    v = fmaxf(v, dpp<kDppXor2>(v));
-    v = fmaxf(v, dpp<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp<kDppMirror>(v));
+    v = max_nn(v, dpp_all<kDppXor1>(v));
+    v = max_nn(v, dpp_all<kDppXor2>(v));
+    v = max_nn(v, dpp_all<kDppHalfMirror>(v));
+    v = max_nn(v, dpp_all<kDppMirror>(v));
     const Pair r = swap16(v);
-    v = fmaxf(r.a, r.b);
+    v = max_nn(r.a, r.b);
     if (!HALVES_EQUAL) {
         const Pair t = swap32(v);
-        v = fmaxf(t.a, t.b);
+        v = max_nn(t.a, t.b);
     }
     return v;
 }
@@ -344,7 +367,7 @@ __device__ __forceinline__ void softmax_weights(int lane, int t_base, int t_end,
 #pragma unroll
     for (int h = 0; h < QPK; ++h) {
         const float sv = own_valid ? s[h] : -INFINITY;
-        const float m_new = fmaxf(st.m[h], wave_max<S::NP == 64>(sv));
+        const float m_new = max_nn(st.m[h], wave_max<S::NP == 64>(sv));
         // arguments <= 0; v_exp_f32 returns 0 for -inf and for results below
         // the fp32 normal range, which weigh nothing at this tolerance
         const float alpha = __builtin_amdgcn_exp2f(st.m[h] - m_new);  // 0 on the first step
@@ -376,22 +399,26 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
     if constexpr (S::PAIRS) {
         // weights of tokens c and c + 16: lanes of rows 0 and 2 hold token
         // c's, rows 1 and 3 token c + 16's
-        const Pair pp = swap16(pw[0]);
+        const Pair pp = swap16(pw[0]);  // 0 for absent tokens
+        st.z[0] = fmaf(pp.a, hi_h(vmetas[0]), st.z[0]);
+        st.z[0] = fmaf(pp.b, hi_h(vmetas[1]), st.z[0]);
+        // One dot2 takes a channel of both tokens: the weights p * step as
+        // a binary16 pair (token c low, c + 16 high), the codes as the same
+        // field of the two tokens' half-words brought into one word.
+        const half2v w2 = pack_h2(pp.a * lo_h(vmetas[0]), pp.b * lo_h(vmetas[1]));
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const float pt = k ? pp.b : pp.a;  // 0 for absent tokens
-            const float ps = pt * lo_h(vmetas[k]);
-            st.z[0] = fmaf(pt, hi_h(vmetas[k]), st.z[0]);
+        for (int u = 0; u < S::WV; ++u) {
+            const uint32_t wa = vwords[u], wb = vwords[S::WV + u];
 #pragma unroll
-            for (int u = 0; u < S::WV; ++u) {
-                const uint32_t word = vwords[k * S::WV + u];
+            for (int hh = 0; hh < 2; ++hh) {
+                // half hh of each token's word: channels hh * TPH .. of word u
+                const uint32_t word = __builtin_amdgcn_perm(wb, wa, hh ? 0x07060302u : 0x05040100u);
                 const uint32_t wsh = word >> C::SHIFT;
 #pragma unroll
                 for (int f = 0; f < C::TPH; ++f) {
-                    const uint32_t m = C::field(word, wsh, f);
-                    st.o[0][u * S::NC + f] = fmaf(ps, lo_h(m), st.o[0][u * S::NC + f]);
-                    st.o[0][u * S::NC + C::TPH + f] =
-                        fmaf(ps, hi_h(m), st.o[0][u * S::NC + C::TPH + f]);
+                    const int cc = u * S::NC + hh * C::TPH + f;
+                    st.o[0][cc] = __builtin_amdgcn_fdot2(
+                        w2, __builtin_bit_cast(half2v, C::field(word, wsh, f)), st.o[0][cc], false);
                 }
             }
         }
