@@ -5,7 +5,9 @@ One step = one decode step for the whole batch of one layer: append the new
 token (key into the full-precision tail, flushed into a quantized group when
 G keys have accumulated; value quantized at once), then decode attention of
 one query per head over every cached token (unpack, dequantize, rotary
-embedding, q.k, online softmax, weighted sum of values).
+embedding, q.k, online softmax, weighted sum of values).  By default a step
+is one kvq_append_attend call (one kernel launch for a plain cache);
+--two-call makes it kvq_append_token then kvq_attend_decode.
 
 The timed steps rotate over R independent caches (R chosen so that R caches
 exceed twice the 256 MB Infinity Cache), so a cache is never still resident
@@ -14,7 +16,8 @@ in that cache when its step starts: the bytes come from HBM.
 Prints one JSON line.  value = decode-attention algorithmic bytes moved per
 second over the timed steps (wall clock, launches included); the roofline
 object reports the attention kernel alone, timed with HIP events on the
-stream it runs on.
+stream it runs on, over as many further steps (events in the timed steps
+would add their own queue packets to the wall clock).
 """
 from __future__ import annotations
 
@@ -32,6 +35,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, vendor figure
 INFINITY_CACHE = 256 << 20  # bytes
 KERNEL_SOURCES = ["quantized_decode_attention_keys_amd/csrc/kvq_attend_kernel.h",
+                  "quantized_decode_attention_keys_amd/csrc/kvq_append.h",
                   "quantized_decode_attention_keys_amd/csrc/kvq_internal.h"]
 TRAFFIC_FILE = "profiles/decode_attention_traffic.json"
 
@@ -262,6 +266,9 @@ def main():
                     help="grouping axes (the ablation flips keys and/or values; no windows)")
     ap.add_argument("--format", default="int", choices=["int", "fp8"],
                     help="fp8: E4M3 bytes for keys and values (8 bits each, no windows)")
+    ap.add_argument("--two-call", action="store_true",
+                    help="step = kvq_append_token then kvq_attend_decode (default: "
+                         "kvq_append_attend, one launch where the cache allows it)")
     ap.add_argument("--no-metrics", action="store_true",
                     help="skip the error-where-consumed metrics of the prompt cache")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -293,7 +300,10 @@ def main():
                            description=cfg.description + "; FP8 E4M3 keys and values")
     n = cfg.n_tokens
     tdt = torch.float16 if cfg.dtype == "float16" else torch.float32
-    total_steps = args.warmup + args.steps
+    # warm-up, the timed steps, then as many again with HIP events around
+    # each launch (the per-launch figures): events add queue packets and
+    # host calls, so the timed steps carry none
+    total_steps = args.warmup + 2 * args.steps
 
     Rw, Sw = args.residual, args.sink
     geom = GEOMETRIES[args.geometry]
@@ -356,6 +366,7 @@ def main():
     vp = [t.data_ptr() for t in v_new]
     qp, op = q.data_ptr(), out.data_ptr()
     append, attend = lib.kvq_append_token, lib.kvq_attend_decode
+    append_attend = lib.kvq_append_attend
 
     hev = HipEvents(2 * args.steps)
     record = hev.hip.hipEventRecord
@@ -364,10 +375,14 @@ def main():
     def step(s, j=None):
         h = handles[s % R]
         i = s // R
-        st = append(h, kp[i], vp[i], stream)
-        if j is not None:
-            st |= record(evp[2 * j], stream)
-        st |= attend(h, qp, op, stream)
+        if args.two_call:
+            st = append(h, kp[i], vp[i], stream)
+            if j is not None:
+                st |= record(evp[2 * j], stream)
+            st |= attend(h, qp, op, stream)
+        else:
+            st = record(evp[2 * j], stream) if j is not None else 0
+            st |= append_attend(h, kp[i], vp[i], qp, op, stream)
         if j is not None:
             st |= record(evp[2 * j + 1], stream)
         return st
@@ -377,28 +392,35 @@ def main():
         status |= step(s)
     torch.cuda.synchronize()
 
+    def step_bytes(L):
+        return fp8_bytes(cfg, L) if fp8 else attend_bytes(cfg, L, Rw, Sw, geom)
+
     lengths = [n - 1 + (args.warmup + j) // R + 1 for j in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
-        status |= step(args.warmup + j, j)
+        status |= step(args.warmup + j)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ev_base = args.warmup + args.steps
+    ev_lengths = [n - 1 + (ev_base + j) // R + 1 for j in range(args.steps)]
+    for j in range(args.steps):
+        status |= step(ev_base + j, j)
+    torch.cuda.synchronize()
     if status != 0:
         raise RuntimeError(f"a library call failed during the timed steps (status bits {status})")
     if [len(c) for c in caches] != [n - 1 + len(range(r, total_steps, R)) for r in range(R)]:
         raise RuntimeError("cache lengths do not match the steps issued")
 
     wall = t1 - t0
-    total_bytes = sum((fp8_bytes(cfg, L) if fp8 else attend_bytes(cfg, L, Rw, Sw, geom))
-                      for L in lengths)
+    total_bytes = sum(step_bytes(L) for L in lengths)
     value = total_bytes / wall / 1e9
     attend_ms = np.array([hev.elapsed_ms(2 * j, 2 * j + 1) for j in range(args.steps)])
     hev.close()
     att_avg_s = float(attend_ms.mean()) / 1e3
-    bytes_per_launch = total_bytes / len(lengths)
+    bytes_per_launch = sum(step_bytes(L) for L in ev_lengths) / len(ev_lengths)
     achieved = bytes_per_launch / att_avg_s / 1e9
-    flops_per_launch = sum(attend_flops(cfg, L) for L in lengths) / len(lengths)
+    flops_per_launch = sum(attend_flops(cfg, L) for L in ev_lengths) / len(ev_lengths)
     achieved_tflops = flops_per_launch / att_avg_s / 1e12
 
     res = {
@@ -423,7 +445,9 @@ def main():
             "sink": Sw,
             "geometry": args.geometry,
             "format": "fp8_e4m3" if fp8 else "int",
-            "context_during_steps": [min(lengths), max(lengths)],
+            "step_calls": ("kvq_append_token + kvq_attend_decode" if args.two_call
+                           else "kvq_append_attend"),
+            "context_during_steps": [min(lengths), max(ev_lengths)],
             "rotating_caches": R,
             "parallelism": "single GPU",
         },
@@ -440,7 +464,12 @@ def main():
             "kernel": ("attend_fp8_kernel (FP8 E4M3 decode attention)" if fp8 else
                        "attend_kernel (decode attention)" if geom == 0 else
                        "attend_geometry_kernel (geometry ablation attention)")
-                      + "; HIP events around each kvq_attend_decode call in the timed loop",
+                      + ("; HIP events around each kvq_attend_decode call, over as many steps"
+                         " after the timed ones"
+                         if args.two_call else
+                         "; HIP events around each kvq_append_attend call (append and attention"
+                         " in one launch for a plain cache), over as many steps after the"
+                         " timed ones"),
             "flops_per_launch": int(flops_per_launch),
             "bytes_per_launch": int(bytes_per_launch),
             "avg_launch_us": round(att_avg_s * 1e6, 3),

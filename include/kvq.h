@@ -238,6 +238,24 @@ int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v,
  * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (n == 0), KVQ_ERR_HIP. */
 int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream);
 
+/* One decode step: kvq_append_token(h, d_k, d_v) followed by
+ * kvq_attend_decode(h, d_q, d_out) over the n + 1 tokens, with the same
+ * arguments, layouts, results and state change (n = n + 1).  The pages
+ * describe exactly this order per generated token: the new key and value
+ * join the cache, then attention reads all of it ("Your KV Cache Doesn't
+ * Have a Bit Problem...", sections "Why the KV Cache Is Where This Bites"
+ * and "The Systems Tax, and Why It Is Not a Detail").  For a cache without
+ * windows (residual == sink == 0), geometry 0, integer codes and at most 4
+ * query heads per KV head, both run in one kernel launch: the block that
+ * reads the newest tokens appends them first.  Otherwise the two calls are
+ * made in turn.  Results equal those of the two calls up to the order of
+ * fp32 additions (the launch may use more waves).
+ * Errors: KVQ_ERR_ARG (a null pointer), KVQ_ERR_CAPACITY (n == max_tokens),
+ * KVQ_ERR_HIP; validation precedes any enqueue.  In the two-call form a
+ * KVQ_ERR_HIP from the attention leaves the append done (n = n + 1). */
+int kvq_append_attend(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
+                      float* d_out, void* stream);
+
 /* Error where it is consumed (the page "Your KV Cache Doesn't Have a Bit
  * Problem...", sections "Keys: The Outliers Live in Fixed Channels" and
  * "Values: Where the Intuition Breaks": validate on attention, not on the

@@ -13,7 +13,7 @@ from ._lib import (  # noqa: F401
     KVQ_VALUES_PER_CHANNEL, KVQ_METRICS, KVQ_FORMAT_INT, KVQ_FORMAT_FP8_E4M3,
     KvqConfig, KvqLayout, KvqError, lib, library_path,
     kvq_workspace_bytes, kvq_create, kvq_quantize_prefill, kvq_append_token,
-    kvq_attend_decode, kvq_error_metrics, kvq_destroy, kvq_length, kvq_get_layout,
-    kvq_layout_for, kvq_strerror,
+    kvq_attend_decode, kvq_append_attend, kvq_error_metrics, kvq_destroy, kvq_length,
+    kvq_get_layout, kvq_layout_for, kvq_strerror,
 )
 from .cache import QuantizedKVCache  # noqa: F401

@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_append_token.restype = ctypes.c_int
         L.kvq_attend_decode.argtypes = [P, P, P, P]
         L.kvq_attend_decode.restype = ctypes.c_int
+        L.kvq_append_attend.argtypes = [P, P, P, P, P, P]
+        L.kvq_append_attend.restype = ctypes.c_int
         L.kvq_error_metrics.argtypes = [P, P, P, P, P, P]
         L.kvq_error_metrics.restype = ctypes.c_int
         L.kvq_destroy.argtypes = [P]
@@ -161,6 +163,10 @@ def kvq_append_token(h: int, d_k: int, d_v: int, stream: int) -> int:
 
 def kvq_attend_decode(h: int, d_q: int, d_out: int, stream: int) -> int:
     return lib().kvq_attend_decode(h, d_q, d_out, stream)
+
+
+def kvq_append_attend(h: int, d_k: int, d_v: int, d_q: int, d_out: int, stream: int) -> int:
+    return lib().kvq_append_attend(h, d_k, d_v, d_q, d_out, stream)
 
 
 def kvq_error_metrics(h: int, d_k: int, d_v: int, d_q: int, d_metrics: int,

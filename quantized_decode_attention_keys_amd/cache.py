@@ -96,6 +96,24 @@ class QuantizedKVCache:
                "kvq_attend_decode")
         return out
 
+    def append_attend(self, k, v, q, out=None, stream=None):
+        """append(k, v) then attend(q) as one decode step (one kernel launch
+        for a plain cache); returns the attention output."""
+        c = self.cfg
+        shape = (c.batch, c.kv_heads, c.head_dim)
+        pk = self._arg(k, shape, "k")
+        pv = self._arg(v, shape, "v")
+        pq = self._arg(q, (c.batch, c.q_heads, c.head_dim), "q")
+        if out is None:
+            out = torch.empty((c.batch, c.q_heads, c.head_dim), dtype=torch.float32,
+                              device=self.device)
+        elif out.dtype != torch.float32 or not out.is_contiguous() or \
+                tuple(out.shape) != (c.batch, c.q_heads, c.head_dim):
+            raise ValueError("out must be a contiguous float32 [batch][q_heads][head_dim] tensor")
+        _check(L.kvq_append_attend(self.handle, pk, pv, pq, out.data_ptr(), self._stream(stream)),
+               "kvq_append_attend")
+        return out
+
     def error_metrics(self, k, v, q, stream=None):
         """Error where it is consumed for the current cache: k, v are the
         unquantized keys and values of all cached tokens

@@ -4,9 +4,9 @@
 namespace kvqi {
 
 hipError_t launch_attend_d64(const Planes& p, const void* q, float* out, int n, int splits,
-                             int waves, hipStream_t stream)
+                             int waves, const void* k_new, const void* v_new, hipStream_t stream)
 {
-    return launch_attend_d<64>(p, q, out, n, splits, waves, stream);
+    return launch_attend_d<64>(p, q, out, n, splits, waves, k_new, v_new, stream);
 }
 
 }  // namespace kvqi

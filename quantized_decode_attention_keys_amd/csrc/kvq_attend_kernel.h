@@ -42,6 +42,7 @@
 // p_t * zero is accumulated once per (token, channel group).
 #pragma once
 
+#include "kvq_append.h"
 #include "kvq_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -593,7 +594,9 @@ __device__ __forceinline__ void softmax_fp_values(int lane, int t_base, int cnt,
 template <int D, int KB, int VB, int QPK>
 __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Planes p, const void* __restrict__ q,
                                                                 float* __restrict__ out, int n,
-                                                                int splits, int hgroups)
+                                                                int splits, int hgroups,
+                                                                const void* __restrict__ k_new,
+                                                                const void* __restrict__ v_new)
 {
     using S = Shape<D, KB, VB, QPK>;
     using KC = Codec<KB>;
@@ -623,6 +626,17 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     const int g0 = gs + (int)((long long)split * ngq / splits);
     const int g1 = gs + (int)((long long)(split + 1) * ngq / splits);
 
+    // Decode step in one launch (k_new != null; plain cache, one block per
+    // (sequence, KV head) and split): the last split's block first appends
+    // token n-1 -- its value quantized per token, its key into the tail and,
+    // when it completes group (n-1)/G, that group quantized.  Everything the
+    // append writes is read only by this block, and only after the barrier
+    // below: the tail and the new value row in the unquantized chunks, the
+    // completed group by the wave whose share holds it (its first loads wait
+    // for the barrier when that group is in its first step).
+    const bool appends = k_new != nullptr && split == splits - 1;
+    const bool flushes = appends && n % G == 0;
+
     // The first step's words go out before anything else: their HBM latency
     // overlaps the query rotation and the twiddle staging.
     HeadPlanes hp;
@@ -633,8 +647,28 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     const int stride = nwaves * S::GPW;
     StepData<KB, S::NVW, S::NVM> cur, nxt;
     int gb = g0 + wave * S::GPW;
-    if (gb < g1)
+    const bool first_late = flushes && gb + S::GPW >= g1;  // the new group is in the first step
+    if (gb < g1 && !first_late)
         load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
+    if (appends && threadIdx.x < D) {  // whole waves: D is a multiple of 64
+        const int c = threadIdx.x;
+        const int t = n - 1;
+        if (p.dtype == 0) {
+            const __half* kn = static_cast<const __half*>(k_new) + bh * D;
+            const __half* vn = static_cast<const __half*>(v_new) + bh * D;
+            append_token_groups<__half, VB>(p.v_codes, p.v_meta, p.tcap, vn, bh, t, c, D);
+            append_channel_groups<__half, KB>(p.k_codes, p.k_meta, p.gcap,
+                                              static_cast<__half*>(p.k_tail) + bh * p.ring * D,
+                                              kn[c], bh, t, c, D);
+        } else {
+            const float* kn = static_cast<const float*>(k_new) + bh * D;
+            const float* vn = static_cast<const float*>(v_new) + bh * D;
+            append_token_groups<float, VB>(p.v_codes, p.v_meta, p.tcap, vn, bh, t, c, D);
+            append_channel_groups<float, KB>(p.k_codes, p.k_meta, p.gcap,
+                                             static_cast<float*>(p.k_tail) + bh * p.ring * D,
+                                             kn[c], bh, t, c, D);
+        }
+    }
 
     // conj(q') * log2(e)/sqrt(D) for this lane's pair, q' = q rotated to n-1
     float2 qc[QPK];
@@ -664,7 +698,9 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         const float sc1 = (float)(1 << (24 - KC::pos((2 * jp + 1) % KC::TPH)));
         twl[idx] = make_float4(t0.x * sc0, -t0.y * sc0, t1.x * sc1, -t1.y * sc1);
     }
-    __syncthreads();
+    __syncthreads();  // also orders the append's global writes before every read of them
+    if (gb < g1 && first_late)
+        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
     // Every wave reads the twiddles from LDS where it uses them: tw_base is
     // re-made opaque every step, so the compiler cannot hoist those reads
     // into 64 registers held for the whole loop.
@@ -695,23 +731,24 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     // step d is in quarter floor(4 d / my_steps): d >= ceil(k my_steps / 4)
     const int q1 = (my_steps + 3) / 4, q2 = (2 * my_steps + 3) / 4, q3 = (3 * my_steps + 3) / 4;
     int done = 0;
+    auto set_priority = [&]() __attribute__((always_inline)) {
+        const int quarter = (done >= q1) + (done >= q2) + (done >= q3);
+        ++done;
+        if (quarter == 0)
+            __builtin_amdgcn_s_setprio(3);
+        else if (quarter == 1)
+            __builtin_amdgcn_s_setprio(2);
+        else if (quarter == 2)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
+    };
     using Step = StepData<KB, S::NVW, S::NVM>;
     // One wave step on the words in `use` while the next step's words load
     // into `fill`; the loop below alternates the two buffers.
     auto step = [&](Step& use, Step& fill) __attribute__((always_inline)) {
         asm volatile("" : "+v"(tw_base));
-        {
-            const int quarter = (done >= q1) + (done >= q2) + (done >= q3);
-            ++done;
-            if (quarter == 0)
-                __builtin_amdgcn_s_setprio(3);
-            else if (quarter == 1)
-                __builtin_amdgcn_s_setprio(2);
-            else if (quarter == 2)
-                __builtin_amdgcn_s_setprio(1);
-            else
-                __builtin_amdgcn_s_setprio(0);
-        }
+        set_priority();
         // unconditional (clamped) prefetch: straight-line code lets the
         // compiler wait only for the current step's loads
         load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, min(gb + stride, g1 - 1), g1, fill);
@@ -1035,48 +1072,48 @@ constexpr size_t attend_lds_bytes(int nwaves)
 
 template <int D, int KB, int VB, int QPK>
 void launch(const Planes& p, const void* q, float* out, int n, int splits, int nwaves,
-            hipStream_t stream)
+            const void* k_new, const void* v_new, hipStream_t stream)
 {
     const int hgroups = p.hq / p.hkv / QPK;
     dim3 grid(splits, p.nb * p.hkv * hgroups);
     nwaves = nwaves < max_block_waves(QPK) ? nwaves : max_block_waves(QPK);
     attend_kernel<D, KB, VB, QPK><<<grid, 64 * nwaves, attend_lds_bytes<D, KB, VB, QPK>(nwaves),
-                                    stream>>>(p, q, out, n, splits, hgroups);
+                                    stream>>>(p, q, out, n, splits, hgroups, k_new, v_new);
     if (splits > 1)
         combine_kernel<D><<<p.nb * p.hq, D, 0, stream>>>(p.partials, p.max_splits, splits, out);
 }
 
 template <int D, int KB, int VB>
 void by_qpk(const Planes& p, const void* q, float* out, int n, int splits, int nwaves,
-            hipStream_t s)
+            const void* k_new, const void* v_new, hipStream_t s)
 {
     switch (p.hq / p.hkv) {
-    case 1: launch<D, KB, VB, 1>(p, q, out, n, splits, nwaves, s); break;
-    case 2: launch<D, KB, VB, 2>(p, q, out, n, splits, nwaves, s); break;
+    case 1: launch<D, KB, VB, 1>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
+    case 2: launch<D, KB, VB, 2>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
     case 4:  // 8 query heads per KV head run as two groups of 4 (registers)
-    case 8: launch<D, KB, VB, 4>(p, q, out, n, splits, nwaves, s); break;
+    case 8: launch<D, KB, VB, 4>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
     }
 }
 
 template <int D, int KB>
 void by_vb(const Planes& p, const void* q, float* out, int n, int splits, int nwaves,
-           hipStream_t s)
+           const void* k_new, const void* v_new, hipStream_t s)
 {
     switch (p.vbits) {
-    case 2: by_qpk<D, KB, 2>(p, q, out, n, splits, nwaves, s); break;
-    case 4: by_qpk<D, KB, 4>(p, q, out, n, splits, nwaves, s); break;
-    case 8: by_qpk<D, KB, 8>(p, q, out, n, splits, nwaves, s); break;
+    case 2: by_qpk<D, KB, 2>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
+    case 4: by_qpk<D, KB, 4>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
+    case 8: by_qpk<D, KB, 8>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
     }
 }
 
 template <int D>
 hipError_t launch_attend_d(const Planes& p, const void* q, float* out, int n, int splits,
-                           int nwaves, hipStream_t s)
+                           int nwaves, const void* k_new, const void* v_new, hipStream_t s)
 {
     switch (p.kbits) {
-    case 2: by_vb<D, 2>(p, q, out, n, splits, nwaves, s); break;
-    case 4: by_vb<D, 4>(p, q, out, n, splits, nwaves, s); break;
-    case 8: by_vb<D, 8>(p, q, out, n, splits, nwaves, s); break;
+    case 2: by_vb<D, 2>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
+    case 4: by_vb<D, 4>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
+    case 8: by_vb<D, 8>(p, q, out, n, splits, nwaves, k_new, v_new, s); break;
     }
     return hipGetLastError();
 }

@@ -331,8 +331,43 @@ int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream)
     int splits, waves;
     attend_shape(h, n, &splits, &waves);
     return hip_status(h->cfg.head_dim == 64
-                          ? kvqi::launch_attend_d64(p, d_q, d_out, n, splits, waves, s)
-                          : kvqi::launch_attend_d128(p, d_q, d_out, n, splits, waves, s));
+                          ? kvqi::launch_attend_d64(p, d_q, d_out, n, splits, waves,
+                                                    nullptr, nullptr, s)
+                          : kvqi::launch_attend_d128(p, d_q, d_out, n, splits, waves,
+                                                     nullptr, nullptr, s));
+}
+
+int kvq_append_attend(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
+                      float* d_out, void* stream)
+{
+    if (!h || !d_k || !d_v || !d_q || !d_out)
+        return KVQ_ERR_ARG;
+    if (h->n >= h->cfg.max_tokens)
+        return KVQ_ERR_CAPACITY;
+    const int qpk_all = h->cfg.q_heads / h->cfg.kv_heads;
+    const bool fused = h->cfg.residual == 0 && h->cfg.sink == 0 && h->cfg.geometry == 0 &&
+                       h->cfg.format == KVQ_FORMAT_INT &&
+                       kvqi::block_heads(qpk_all) == qpk_all;  // one block per KV head
+    if (!fused) {
+        const int st = kvq_append_token(h, d_k, d_v, stream);
+        return st != KVQ_OK ? st : kvq_attend_decode(h, d_q, d_out, stream);
+    }
+    const int n = h->n + 1;
+    const kvqi::Planes p = planes_of(h);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int splits, waves;
+    attend_shape(h, n, &splits, &waves);
+    const int append_waves = h->cfg.head_dim / 64;  // threads 0..head_dim-1 append
+    if (waves < append_waves)
+        waves = append_waves;
+    const int st = hip_status(h->cfg.head_dim == 64
+                                  ? kvqi::launch_attend_d64(p, d_q, d_out, n, splits, waves,
+                                                            d_k, d_v, s)
+                                  : kvqi::launch_attend_d128(p, d_q, d_out, n, splits, waves,
+                                                             d_k, d_v, s));
+    if (st == KVQ_OK)
+        h->n = n;
+    return st;
 }
 
 int kvq_error_metrics(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,

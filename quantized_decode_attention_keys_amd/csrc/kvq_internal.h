@@ -73,10 +73,16 @@ hipError_t launch_quantize_prefill(const Planes& p, const void* k, const void* v
                                    int n_tokens, hipStream_t stream);
 hipError_t launch_append(const Planes& p, const void* k, const void* v, int n,
                          hipStream_t stream);
+// Decode attention over n tokens (kvq_attend_d64.hip, kvq_attend_d128.hip).
+// With k_new and v_new non-null (plain cache: no windows, geometry 0,
+// integer codes; one block per (sequence, KV head) and split), the kernel
+// first appends token n-1 from them, as launch_append with n-1 would.
 hipError_t launch_attend_d64(const Planes& p, const void* q, float* out, int n,
-                             int splits, int waves, hipStream_t stream);
+                             int splits, int waves, const void* k_new, const void* v_new,
+                             hipStream_t stream);
 hipError_t launch_attend_d128(const Planes& p, const void* q, float* out, int n,
-                              int splits, int waves, hipStream_t stream);
+                              int splits, int waves, const void* k_new, const void* v_new,
+                              hipStream_t stream);
 // Attention over a cache with a non-zero geometry (kvq_geometry.hip).
 hipError_t launch_attend_geometry(const Planes& p, const void* q, float* out, int n,
                                   int splits, hipStream_t stream);

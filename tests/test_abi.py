@@ -168,6 +168,7 @@ def test_null_handle_calls():
     assert L.kvq_quantize_prefill(None, 1, 1, 4, None) == L.KVQ_ERR_ARG
     assert L.kvq_append_token(None, 1, 1, None) == L.KVQ_ERR_ARG
     assert L.kvq_attend_decode(None, 1, 1, None) == L.KVQ_ERR_ARG
+    assert L.kvq_append_attend(None, 1, 1, 1, 1, None) == L.KVQ_ERR_ARG
     assert L.kvq_error_metrics(None, 1, 1, 1, 1, None) == L.KVQ_ERR_ARG
 
 
