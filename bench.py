@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, vendor figure
+FP32_UNPACKED_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12  # 78.6: one FMA per lane per cycle
 INFINITY_CACHE = 256 << 20  # bytes
 KERNEL_SOURCES = ["quantized_decode_attention_keys_amd/csrc/kvq_attend_kernel.h",
                   "quantized_decode_attention_keys_amd/csrc/kvq_append.h",
@@ -477,6 +478,11 @@ def main():
                            round(float(np.percentile(attend_ms, 90)) * 1e3, 3)],
             "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4)},
+            # the fp32 vector peak above counts packed FMAs (two per lane per
+            # cycle); code built without packed fp32 issues one per lane per
+            # cycle: 256 CUs x 64 lanes x 2 flops x 2.4 GHz
+            "fp32_unpacked": {"peak": FP32_UNPACKED_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(achieved_tflops / FP32_UNPACKED_PEAK_TFLOPS, 4)},
         },
         "prefill": {
             "tokens": n - 1,

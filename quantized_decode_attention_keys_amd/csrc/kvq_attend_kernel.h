@@ -26,8 +26,8 @@
 //     = Re[ T_j (Q_g (x + i y)) ],  T_j = e^{i j theta_i},  Q_g = conj(q'_i) e^{i gG theta_i},
 // so per (group, pair) six constants fold dequantization and the group
 // rotation, and per token the lane spends 4 FMAs on Q_g (x + i y) and 2 on
-// the per-token twiddle T_j, which stays in registers for the whole kernel.
-// The 32 per-pair partial scores are summed across lanes through LDS.
+// the per-token twiddle T_j, staged once per block in LDS.  The 32
+// per-pair partial scores are summed across lanes through LDS.
 //
 // Code unpacking.  A B-bit field masked in place inside a 16-bit half of a
 // code word, with its lowest bit at position e <= 9, is the binary16 bit
@@ -37,15 +37,21 @@
 // per-token twiddle (keys) or into one rescale at the end (values), so a
 // 32-bit word of codes costs one AND per two codes plus one shift.
 //
-// Value side: lane = one 32-bit code word of a token row (32/B channels) x a
-// token slot; the per-token weight p_t * step multiplies the codes and
-// p_t * zero is accumulated once per (token, channel group).
+// Value side: the per-token weight p_t * step multiplies the codes and
+// p_t * zero is accumulated once per (token, channel group).  With head_dim
+// 128 a lane takes whole channel groups of two (or four) tokens, and
+// v_dot2_f32_f16 adds the products of two tokens at once: the weights as a
+// binary16 pair, the two tokens' codes of a channel as the same field of
+// one word (see softmax_values).  With head_dim 64 a lane takes one 32-bit
+// code word of a token row (32/B channels) per token slot.
 #pragma once
 
 #include "kvq_append.h"
 #include "kvq_internal.h"
 
 #include <hip/hip_fp16.h>
+
+#include <type_traits>
 
 namespace kvqi {
 namespace {
@@ -426,6 +432,11 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
         return;
     }
     if constexpr (S::QUADS) {
+        // Token slots k = 0..3 are tokens c, c^8, c+16, (c^8)+16; slots k and
+        // k + 2 go through v_dot2_f32_f16 together, as in the one-head
+        // variant: their half-words brought into one word by one perm (shared
+        // by every head), their weights p * step as one binary16 pair.
+        half2v w2[QPK][2];
 #pragma unroll
         for (int h = 0; h < QPK; ++h) {
             // tokens c and c + 16 from the row pair, c^8 and (c^8) + 16 by
@@ -433,20 +444,29 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
             const Pair pp = swap16(pw[h]);
             const float pk[4] = {pp.a, dpp<kDppRor8>(pp.a), pp.b, dpp<kDppRor8>(pp.b)};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float pt = pk[k];  // 0 for absent tokens
-                const float ps = pt * lo_h(vmetas[k]);
-                st.z[h] = fmaf(pt, hi_h(vmetas[k]), st.z[h]);
+            for (int k = 0; k < 4; ++k)
+                st.z[h] = fmaf(pk[k], hi_h(vmetas[k]), st.z[h]);  // 0 for absent tokens
 #pragma unroll
-                for (int u = 0; u < S::NW; ++u) {
-                    const uint32_t word = vwords[k * S::NW + u];
+            for (int k = 0; k < 2; ++k)
+                w2[h][k] = pack_h2(pk[k] * lo_h(vmetas[k]), pk[k + 2] * lo_h(vmetas[k + 2]));
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+#pragma unroll
+            for (int u = 0; u < S::NW; ++u) {
+                const uint32_t wa = vwords[k * S::NW + u], wb = vwords[(k + 2) * S::NW + u];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t word =
+                        __builtin_amdgcn_perm(wb, wa, hh ? 0x07060302u : 0x05040100u);
                     const uint32_t wsh = word >> C::SHIFT;
 #pragma unroll
                     for (int f = 0; f < C::TPH; ++f) {
-                        const uint32_t m = C::field(word, wsh, f);
-                        st.o[h][u * S::NC + f] = fmaf(ps, lo_h(m), st.o[h][u * S::NC + f]);
-                        st.o[h][u * S::NC + C::TPH + f] =
-                            fmaf(ps, hi_h(m), st.o[h][u * S::NC + C::TPH + f]);
+                        const half2v m = __builtin_bit_cast(half2v, C::field(word, wsh, f));
+                        const int cc = u * S::NC + hh * C::TPH + f;
+#pragma unroll
+                        for (int h = 0; h < QPK; ++h)
+                            st.o[h][cc] = __builtin_amdgcn_fdot2(w2[h][k], m, st.o[h][cc], false);
                     }
                 }
             }
@@ -937,20 +957,39 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     float* so = smem + 2 * kMaxWaves * QPK;     // [nwaves][QPK][D]
     if constexpr (S::PAIRS) {
         // lane (r, c) holds channel group r over its tokens: sum the 16
-        // lanes of row r per channel
+        // lanes of row r per channel by halving exchanges -- at each stage
+        // a lane keeps half of its channels and adds its partner's values
+        // of that half (partners: mirror, half mirror, xor 2, xor 1, each
+        // pairing lanes that differ in bit 3, 2, 1, 0), so lane c ends with
+        // channels 2c and 2c + 1 of the group.  The zero-point terms are the
+        // same for every channel of the row: summed once.
         const float L = wave_sum(st.l[0]);
-        const int r = lane >> 4;
+        const int r = lane >> 4, c16 = lane & 15;
+        float zs = st.z[0];
+        zs += dpp<kDppXor1>(zs);
+        zs += dpp<kDppXor2>(zs);
+        zs += dpp<kDppHalfMirror>(zs);
+        zs += dpp<kDppMirror>(zs);
+        float v[G];
 #pragma unroll
-        for (int c = 0; c < G; ++c) {
-            const float sc = (float)(1 << (24 - VC::pos(c % VC::TPH)));
-            float x = fmaf(st.o[0][c], sc, st.z[0]);
-            x += dpp<kDppXor1>(x);
-            x += dpp<kDppXor2>(x);
-            x += dpp<kDppHalfMirror>(x);
-            x += dpp<kDppMirror>(x);
-            if ((lane & 15) == 0)
-                so[wave * D + r * G + c] = x;
-        }
+        for (int c = 0; c < G; ++c)
+            v[c] = st.o[0][c];
+        auto halve = [&](auto ctrl, int half, bool upper) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < half; ++i) {
+                const float keep = upper ? v[i + half] : v[i];
+                const float send = upper ? v[i] : v[i + half];
+                v[i] = keep + dpp_all<decltype(ctrl)::value>(send);
+            }
+        };
+        halve(std::integral_constant<int, kDppMirror>{}, 16, (c16 & 8) != 0);
+        halve(std::integral_constant<int, kDppHalfMirror>{}, 8, (c16 & 4) != 0);
+        halve(std::integral_constant<int, kDppXor2>{}, 4, (c16 & 2) != 0);
+        halve(std::integral_constant<int, kDppXor1>{}, 2, (c16 & 1) != 0);
+        float2 x;
+        x.x = fmaf(v[0], (float)(1 << (24 - VC::pos((2 * c16) % VC::TPH))), zs);
+        x.y = fmaf(v[1], (float)(1 << (24 - VC::pos((2 * c16 + 1) % VC::TPH))), zs);
+        *reinterpret_cast<float2*>(so + wave * D + r * G + 2 * c16) = x;
         if (lane == 0) {
             sm[wave] = st.m[0];
             sl[wave] = L;
