@@ -651,14 +651,9 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     // token n-1 -- its value quantized per token, its key into the tail and,
     // when it completes group (n-1)/G, that group quantized.  Everything the
     // append writes is read only by this block, and only after the barrier
-    // below: the tail and the new value row in the unquantized chunks, the
-    // completed group by the wave whose share holds it (its first loads wait
-    // for the barrier when that group is in its first step).
+    // below (every load of cache words comes after it).
     const bool appends = k_new != nullptr && split == splits - 1;
-    const bool flushes = appends && n % G == 0;
 
-    // The first step's words go out before anything else: their HBM latency
-    // overlaps the query rotation and the twiddle staging.
     HeadPlanes hp;
     hp.kc = p.k_codes + bh * (size_t)p.gcap * D * S::WK;
     hp.km = p.k_meta + bh * (size_t)p.gcap * D;
@@ -667,9 +662,6 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     const int stride = nwaves * S::GPW;
     StepData<KB, S::NVW, S::NVM> cur, nxt;
     int gb = g0 + wave * S::GPW;
-    const bool first_late = flushes && gb + S::GPW >= g1;  // the new group is in the first step
-    if (gb < g1 && !first_late)
-        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
     if (appends && threadIdx.x < D) {  // whole waves: D is a multiple of 64
         const int c = threadIdx.x;
         const int t = n - 1;
@@ -719,8 +711,6 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         twl[idx] = make_float4(t0.x * sc0, -t0.y * sc0, t1.x * sc1, -t1.y * sc1);
     }
     __syncthreads();  // also orders the append's global writes before every read of them
-    if (gb < g1 && first_late)
-        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
     // Every wave reads the twiddles from LDS where it uses them: tw_base is
     // re-made opaque every step, so the compiler cannot hoist those reads
     // into 64 registers held for the whole loop.
@@ -747,7 +737,11 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     // share long before the youngest, which then runs alone at a fraction of
     // the SIMD's issue rate.  Each wave lowers its priority by one level per
     // quarter of its share done, so the waves of a SIMD finish together.
-    const int my_steps = gb < g1 ? (g1 - 1 - gb) / stride + 1 : 0;
+    // a wave's share: its chunks of unquantized tokens (last split only),
+    // then its groups
+    const int chunk0 = split == splits - 1 ? nwaves - 1 - wave : nchunks;
+    const int my_chunks = chunk0 < nchunks ? (nchunks - 1 - chunk0) / nwaves + 1 : 0;
+    const int my_steps = my_chunks + (gb < g1 ? (g1 - 1 - gb) / stride + 1 : 0);
     // step d is in quarter floor(4 d / my_steps): d >= ceil(k my_steps / 4)
     const int q1 = (my_steps + 3) / 4, q2 = (2 * my_steps + 3) / 4, q3 = (3 * my_steps + 3) / 4;
     int done = 0;
@@ -875,22 +869,17 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, use.vw, use.vm, st);
         gb += stride;
     };
-    while (gb < g1) {
-        step(cur, nxt);
-        if (gb >= g1)
-            break;
-        step(nxt, cur);
-    }
-
-    __builtin_amdgcn_s_setprio(0);
-
-    for (int ch = nwaves - 1 - wave; split == splits - 1 && ch < nchunks; ch += nwaves) {
+    // Unquantized chunks first (last split only): they then run beside the
+    // other waves' groups, paced by the priorities, instead of alone after
+    // them.  A wave's first group is loaded after its chunks, so no group's
+    // words are held in registers across the chunk code.
+    for (int ch = chunk0; ch < nchunks; ch += nwaves) {
         asm volatile("" : "+v"(tw_base));  // keep the twiddle reads in the loop
+        set_priority();
         // One chunk of unquantized tokens t0 .. t0+cnt-1, from the sinks or
         // the rings (rows from row0, contiguous: the ring and t0 are
-        // multiples of G), scored like one more group after the quantized
-        // ones (the softmax is order-free): lane = channel pair, the tokens
-        // across its registers.
+        // multiples of G), scored like one more group (the softmax is
+        // order-free): lane = channel pair, the tokens across its registers.
         const bool in_sink = ch < nsink_chunks;
         const int t0 = in_sink ? ch * G : tq + (ch - nsink_chunks) * G;
         const int cnt = min(G, (in_sink ? ns : n) - t0);
@@ -949,6 +938,17 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
             softmax_values<D, KB, VB, QPK>(lane, t0, n, s, vw, vm, st);
         }
     }
+
+    if (gb < g1)
+        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
+    while (gb < g1) {
+        step(cur, nxt);
+        if (gb >= g1)
+            break;
+        step(nxt, cur);
+    }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- merge the waves of this block
     __syncthreads();  // every wave is done with its reduce buffer

@@ -1,8 +1,9 @@
 """GPU parity at the full sizes of the larger workloads, in the launch
-configuration the bench uses (the library picks splits and waves from the
-shape).  Codes, metadata and tail bit-exact for sampled sequences; attention
-within 2e-3 of max|out| for sampled (sequence, head) rows, computed by the
-oracle from the same seeded inputs."""
+configuration the bench uses: each decode step is one kvq_append_attend call
+(the library picks splits and waves from the shape).  Codes, metadata and
+tail bit-exact for sampled sequences; attention within 2e-3 of max|out| for
+sampled (sequence, head) rows, computed by the oracle from the same seeded
+inputs."""
 import numpy as np
 import pytest
 import torch
@@ -33,8 +34,9 @@ def _check_rows(cfg, out, q, planes, b, n, heads=None):
 
 
 def test_llama2_13b_decode_loop():
-    """Prefill 8192 tokens, then 64 steps of append + attend (n = 8193 ...
-    8256, key groups flushed from the tail at steps 32 and 64)."""
+    """Prefill 8192 tokens, then 64 decode steps, each appending one token
+    and attending in one launch (n = 8193 ... 8256, key groups flushed from
+    the tail at steps 32 and 64)."""
     cfg = synth.CONFIGS["llama2_13b"]
     n0, steps = 8192, 64
     cap = n0 + steps
@@ -46,9 +48,9 @@ def test_llama2_13b_decode_loop():
     planes_at = {}
     outs = {}
     for s in range(1, steps + 1):
-        cache.append(k_new[:, :, s - 1].contiguous(), v_new[:, :, s - 1].contiguous())
         q = synth.make_query(cfg, 0, s)
-        out = cache.attend(to_gpu(q))
+        out = cache.append_attend(k_new[:, :, s - 1].contiguous(),
+                                  v_new[:, :, s - 1].contiguous(), to_gpu(q))
         if s in (1, 31, 32, 33, 63, 64):
             outs[s] = (q, out.cpu().numpy())
     torch.cuda.synchronize()
@@ -67,9 +69,12 @@ def test_llama2_13b_b4_sampled():
     cfg = synth.CONFIGS["llama2_13b_b4"]
     n = cfg.n_tokens
     cache = make_cache(cfg, n)
-    cache.prefill(to_gpu(synth.make_keys(cfg, 0, 0, n)), to_gpu(synth.make_values(cfg, 0, 0, n)))
+    cache.prefill(to_gpu(synth.make_keys(cfg, 0, 0, n - 1)),
+                  to_gpu(synth.make_values(cfg, 0, 0, n - 1)))
     q = synth.make_query(cfg, 0, 0)
-    out = cache.attend(to_gpu(q)).cpu().numpy()
+    out = cache.append_attend(to_gpu(synth.make_keys(cfg, 0, n - 1, n)[:, :, 0]),
+                              to_gpu(synth.make_values(cfg, 0, n - 1, n)[:, :, 0]),
+                              to_gpu(q)).cpu().numpy()
     gp = gpu_planes(cache)
     b = 9
     op = _oracle_seq_planes(cfg, b, n, n)
@@ -78,9 +83,9 @@ def test_llama2_13b_b4_sampled():
 
 
 def test_long_context_sampled():
-    """131071-token prompt plus one appended token (n = 131072, keys at 4
-    bits, values at 2), split over many blocks and merged by the combine
-    kernel."""
+    """131071-token prompt plus one decode step (n = 131072, keys at 4
+    bits, values at 2), split over many blocks (the last one appends) and
+    merged by the combine kernel."""
     cfg = synth.CONFIGS["long"]
     n = cfg.n_tokens
     cache = make_cache(cfg, n)
@@ -88,9 +93,8 @@ def test_long_context_sampled():
                   to_gpu(synth.make_values(cfg, 0, 0, n - 1)))
     last_k = to_gpu(synth.make_keys(cfg, 0, n - 1, n)[:, :, 0])
     last_v = to_gpu(synth.make_values(cfg, 0, n - 1, n)[:, :, 0])
-    cache.append(last_k, last_v)
     q = synth.make_query(cfg, 0, 0)
-    out = cache.attend(to_gpu(q)).cpu().numpy()
+    out = cache.append_attend(last_k, last_v, to_gpu(q)).cpu().numpy()
     gp = gpu_planes(cache)
     op = _oracle_seq_planes(cfg, 0, n, n)
     assert_planes_equal(gp, op, n)
@@ -98,7 +102,8 @@ def test_long_context_sampled():
 
 
 def test_long_context_ragged_tail():
-    """The long workload with a 31-token tail (n = 131071)."""
+    """The long workload with a 31-token tail (n = 131071), attention alone
+    (kvq_attend_decode) after the prefill."""
     cfg = synth.scaled(synth.CONFIGS["long"], n_tokens=131071)
     n = cfg.n_tokens
     cache = make_cache(cfg, n)
@@ -116,10 +121,10 @@ def test_gqa_sampled():
     cache = make_cache(cfg, n)
     cache.prefill(to_gpu(synth.make_keys(cfg, 0, 0, n - 1)),
                   to_gpu(synth.make_values(cfg, 0, 0, n - 1)))
-    cache.append(to_gpu(synth.make_keys(cfg, 0, n - 1, n)[:, :, 0]),
-                 to_gpu(synth.make_values(cfg, 0, n - 1, n)[:, :, 0]))
     q = synth.make_query(cfg, 0, 0)
-    out = cache.attend(to_gpu(q)).cpu().numpy()
+    out = cache.append_attend(to_gpu(synth.make_keys(cfg, 0, n - 1, n)[:, :, 0]),
+                              to_gpu(synth.make_values(cfg, 0, n - 1, n)[:, :, 0]),
+                              to_gpu(q)).cpu().numpy()
     gp = gpu_planes(cache)
     b = 41
     op = _oracle_seq_planes(cfg, b, n, n)
