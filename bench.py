@@ -6,8 +6,9 @@ token (key into the full-precision tail, flushed into a quantized group when
 G keys have accumulated; value quantized at once), then decode attention of
 one query per head over every cached token (unpack, dequantize, rotary
 embedding, q.k, online softmax, weighted sum of values).  By default a step
-is one kvq_append_attend call (one kernel launch for a plain cache);
---two-call makes it kvq_append_token then kvq_attend_decode.
+is one kvq_append_attend call where that is one kernel launch (a plain cache
+with at most 4 query heads per KV head), else kvq_append_token then
+kvq_attend_decode; --two-call always makes the two calls.
 
 The timed steps rotate over R independent caches (R chosen so that R caches
 exceed twice the 256 MB Infinity Cache), so a cache is never still resident
@@ -269,7 +270,8 @@ def main():
                     help="fp8: E4M3 bytes for keys and values (8 bits each, no windows)")
     ap.add_argument("--two-call", action="store_true",
                     help="step = kvq_append_token then kvq_attend_decode (default: "
-                         "kvq_append_attend, one launch where the cache allows it)")
+                         "kvq_append_attend where it is one launch, i.e. a plain cache with "
+                         "at most 4 query heads per KV head; the two calls otherwise)")
     ap.add_argument("--no-metrics", action="store_true",
                     help="skip the error-where-consumed metrics of the prompt cache")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -373,10 +375,18 @@ def main():
     record = hev.hip.hipEventRecord
     evp = hev.ev
 
+    # kvq_append_attend runs as one launch only for a plain cache with at
+    # most 4 query heads per KV head; otherwise it makes the two calls, and
+    # the bench then makes them itself so that the events time the
+    # attention launch alone
+    one_launch = (Rw == 0 and Sw == 0 and geom == 0 and not fp8
+                  and cfg.q_heads // cfg.kv_heads <= 4)
+    two_call = args.two_call or not one_launch
+
     def step(s, j=None):
         h = handles[s % R]
         i = s // R
-        if args.two_call:
+        if two_call:
             st = append(h, kp[i], vp[i], stream)
             if j is not None:
                 st |= record(evp[2 * j], stream)
@@ -446,7 +456,7 @@ def main():
             "sink": Sw,
             "geometry": args.geometry,
             "format": "fp8_e4m3" if fp8 else "int",
-            "step_calls": ("kvq_append_token + kvq_attend_decode" if args.two_call
+            "step_calls": ("kvq_append_token + kvq_attend_decode" if two_call
                            else "kvq_append_attend"),
             "context_during_steps": [min(lengths), max(ev_lengths)],
             "rotating_caches": R,
@@ -467,7 +477,7 @@ def main():
                        "attend_geometry_kernel (geometry ablation attention)")
                       + ("; HIP events around each kvq_attend_decode call, over as many steps"
                          " after the timed ones"
-                         if args.two_call else
+                         if two_call else
                          "; HIP events around each kvq_append_attend call (append and attention"
                          " in one launch for a plain cache), over as many steps after the"
                          " timed ones"),
