@@ -15,7 +15,9 @@
 // (W from the launch).  Each wave takes whole key groups in turn (waves never
 // wait on each other inside the loop), keeps its own online-softmax state,
 // and prefetches the next group's key and value words while it computes the
-// current one.  The block merges its waves at the end; with one split it
+// current one (in the one-head head_dim-128 variants with 2-bit values the
+// values lag one step: a step scores its group and adds the previous
+// group's values).  The block merges its waves at the end; with one split it
 // writes the output, otherwise (o, m, l) partials for the combine kernel.
 //
 // Key side, one group of 32 tokens: lane = channel pair i (64 pairs for
@@ -341,9 +343,9 @@ __device__ __forceinline__ void load_values(const HeadPlanes& hp, int lane, int 
 }
 
 // Key words, metadata and group rotation of key group gb (and gb + 1 for
-// head_dim 64) plus the value words of its tokens; gb <= g1 - 1.
+// head_dim 64); gb <= g1 - 1.
 template <int D, int KB, int VB, int QPK>
-__device__ __forceinline__ void load_step(
+__device__ __forceinline__ void load_keys(
     const HeadPlanes& hp, const float2* __restrict__ rope_group, int lane, int gb, int g1,
     StepData<KB, Shape<D, KB, VB, QPK>::NVW, Shape<D, KB, VB, QPK>::NVM>& sd)
 {
@@ -355,7 +357,6 @@ __device__ __forceinline__ void load_step(
     load_words<2 * S::WK>(hp.kc + (size_t)gb * (D * S::WK) + ci * S::WK, sd.kw);
     sd.km = *reinterpret_cast<const uint2*>(hp.km + (size_t)gb * D + ci);
     sd.rg = rope_group[(size_t)gb * S::NP + gl * S::NP + i];
-    load_values<D, KB, VB, QPK, (S::GPW > 1)>(hp, lane, gb * G, g1 * G - 1, sd.vw, sd.vm);
 }
 
 // Online-softmax update for one wave step.  Lane `lane` holds score s[h] of
@@ -391,18 +392,15 @@ __device__ __forceinline__ void softmax_weights(int lane, int t_base, int t_end,
     }
 }
 
-// Softmax update for one wave step and accumulation of its value tokens from
-// their code words (absent tokens' words may be anything: they weigh 0).
+// Accumulation of one wave step's value tokens from their code words with
+// their softmax weights pw (absent tokens weigh 0, whatever their words).
 template <int D, int KB, int VB, int QPK>
-__device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
-                                               const float (&s)[QPK], const uint32_t* vwords,
-                                               const uint32_t* vmetas,
-                                               WaveState<QPK, Shape<D, KB, VB, QPK>::NCL>& st)
+__device__ __forceinline__ void accumulate_values(int lane, const float (&pw)[QPK],
+                                                  const uint32_t* vwords, const uint32_t* vmetas,
+                                                  WaveState<QPK, Shape<D, KB, VB, QPK>::NCL>& st)
 {
     using S = Shape<D, KB, VB, QPK>;
     using C = Codec<VB>;
-    float pw[QPK];
-    softmax_weights<D, KB, VB, QPK>(lane, t_base, t_end, s, pw, st);
     if constexpr (S::PAIRS) {
         // weights of tokens c and c + 16: lanes of rows 0 and 2 hold token
         // c's, rows 1 and 3 token c + 16's
@@ -492,6 +490,18 @@ __device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
             }
         }
     }
+}
+
+// Softmax update for one wave step and accumulation of its value tokens.
+template <int D, int KB, int VB, int QPK>
+__device__ __forceinline__ void softmax_values(int lane, int t_base, int t_end,
+                                               const float (&s)[QPK], const uint32_t* vwords,
+                                               const uint32_t* vmetas,
+                                               WaveState<QPK, Shape<D, KB, VB, QPK>::NCL>& st)
+{
+    float pw[QPK];
+    softmax_weights<D, KB, VB, QPK>(lane, t_base, t_end, s, pw, st);
+    accumulate_values<D, KB, VB, QPK>(lane, pw, vwords, vmetas, st);
 }
 
 // N consecutive elements of an fp16 (dtype 0) or fp32 row as floats; N a
@@ -609,6 +619,14 @@ __device__ __forceinline__ void softmax_fp_values(int lane, int t_base, int cnt,
             }
         }
     }
+}
+
+// Variants whose values lag their keys by one step (the one-head head_dim-128
+// variants with 2-bit values): deferring the others' values spilled registers
+// (GQA 589 -> 870 us, 13B at 4/4 bits 178 -> 185 us; 7B 37.5 -> 36.9 us).
+constexpr bool defers_values(int kb, int vb, int qpk, int np)
+{
+    return qpk == 1 && vb == 2 && np == 64 && kb <= 8;
 }
 
 // Variants whose unquantized chunks are scored before their groups: those
@@ -763,14 +781,34 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
             __builtin_amdgcn_s_setprio(0);
     };
     using Step = StepData<KB, S::NVW, S::NVM>;
+    // With kDefer, values lag the keys by one step: a step scores its
+    // group's keys and adds the previous group's values, so the first step
+    // waits for key words only (half the first burst of loads).
+    constexpr bool kDefer = defers_values(KB, VB, QPK, NP);
+    float pw_prev[QPK];
+    bool has_prev = false;
     // One wave step on the words in `use` while the next step's words load
     // into `fill`; the loop below alternates the two buffers.
     auto step = [&](Step& use, Step& fill) __attribute__((always_inline)) {
         asm volatile("" : "+v"(tw_base));
         set_priority();
-        // unconditional (clamped) prefetch: straight-line code lets the
-        // compiler wait only for the current step's loads
-        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, min(gb + stride, g1 - 1), g1, fill);
+        // unconditional (clamped) prefetch of the next step's words:
+        // straight-line code lets the compiler wait only for the loads each
+        // part uses.  With deferred values, `fill` takes the next step's keys
+        // and this step's values, and the previous step's values are added
+        // now, with the weights that step computed (relative to the running
+        // maximum before this step's rescale).
+        const int gnext = min(gb + stride, g1 - 1);
+        load_keys<D, KB, VB, QPK>(hp, p.rope_group, lane, gnext, g1, fill);
+        if constexpr (kDefer) {
+            load_values<D, KB, VB, QPK, (S::GPW > 1)>(hp, lane, gb * G, g1 * G - 1, fill.vw,
+                                                      fill.vm);
+            if (has_prev)
+                accumulate_values<D, KB, VB, QPK>(lane, pw_prev, use.vw, use.vm, st);
+        } else {
+            load_values<D, KB, VB, QPK, (S::GPW > 1)>(hp, lane, gnext * G, g1 * G - 1, fill.vw,
+                                                      fill.vm);
+        }
         const float s0 = h2f(use.km.x), z0 = h2f(use.km.x >> 16);
         const float s1 = h2f(use.km.y), z1 = h2f(use.km.y >> 16);
         float s[QPK];
@@ -871,7 +909,12 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 s[h] = acc;
             }
         }
-        softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, use.vw, use.vm, st);
+        if constexpr (kDefer) {
+            softmax_weights<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, pw_prev, st);
+            has_prev = true;
+        } else {
+            softmax_values<D, KB, VB, QPK>(lane, gb * G, g1 * G, s, use.vw, use.vm, st);
+        }
         gb += stride;
     };
     // Unquantized chunks (last split only).  Where the variant's registers
@@ -946,14 +989,24 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
             }
         }
     }
-    if (gb < g1)
-        load_step<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
+    if (gb < g1) {
+        load_keys<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
+        if constexpr (!kDefer)
+            load_values<D, KB, VB, QPK, (S::GPW > 1)>(hp, lane, gb * G, g1 * G - 1, cur.vw,
+                                                      cur.vm);
+    }
+    bool last_in_nxt = false;  // which buffer holds the last step's values
     while (gb < g1) {
         step(cur, nxt);
+        last_in_nxt = true;
         if (gb >= g1)
             break;
         step(nxt, cur);
+        last_in_nxt = false;
     }
+    if (kDefer && has_prev)
+        accumulate_values<D, KB, VB, QPK>(lane, pw_prev, last_in_nxt ? nxt.vw : cur.vw,
+                                          last_in_nxt ? nxt.vm : cur.vm, st);
     if constexpr (!chunks_first(KB, VB, QPK)) {  // the same chunks, after the groups
         for (int ch = chunk0; ch < nchunks; ch += nwaves) {
             asm volatile("" : "+v"(tw_base));  // keep the twiddle reads in the loop
