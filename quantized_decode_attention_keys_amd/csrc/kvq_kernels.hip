@@ -34,15 +34,15 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h)
 // tokens down the channel, so the per-channel statistics need no cross-lane
 // reduction; consecutive threads read consecutive channels of a token row.
 template <typename T, int BITS>
-__global__ __launch_bounds__(256) void quant_keys_kernel(Planes p, const T* __restrict__ k,
-                                                         int n_tokens, int g_begin, int g_end)
+__device__ __forceinline__ void quant_keys_block(const Planes& p, const T* __restrict__ k,
+                                                 int n_tokens, int g_begin, int g_end, int bx,
+                                                 size_t bh)
 {
     constexpr int WK = G * BITS / 32;
     const int D = p.D;
     const int gpb = blockDim.x / D;
     const int c = threadIdx.x % D;
-    const int g = g_begin + blockIdx.x * gpb + threadIdx.x / D;
-    const size_t bh = blockIdx.y;
+    const int g = g_begin + bx * gpb + threadIdx.x / D;
     if (g >= g_end)
         return;
     const T* src = k + (bh * (size_t)n_tokens + (size_t)g * G) * D + c;
@@ -58,6 +58,13 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(Planes p, const T* __re
     for (int i = 0; i < WK; ++i)
         dst[i] = w[i];
     p.k_meta[gc] = meta;
+}
+
+template <typename T, int BITS>
+__global__ __launch_bounds__(256) void quant_keys_kernel(Planes p, const T* __restrict__ k,
+                                                         int n_tokens, int g_begin, int g_end)
+{
+    quant_keys_block<T, BITS>(p, k, n_tokens, g_begin, g_end, blockIdx.x, blockIdx.y);
 }
 
 // Copy tokens [t0, t1) of each sequence/head verbatim into a buffer of
@@ -83,12 +90,11 @@ __global__ void copy_tail_kernel(Planes p, const T* __restrict__ src, T* __restr
 // Input tokens [0, n_src) of rows of src_stride tokens go to cache slots
 // [t_dst0, t_dst0 + n_src).
 template <typename T, int BITS>
-__global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __restrict__ v,
-                                                           int n_src, int src_stride, int t_dst0,
-                                                           size_t total)
+__device__ __forceinline__ void quant_values_thread(const Planes& p, const T* __restrict__ v,
+                                                    int n_src, int src_stride, int t_dst0,
+                                                    size_t total, size_t idx)
 {
     constexpr int WV = G * BITS / 32;
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total)
         return;
     const int D = p.D;
@@ -110,6 +116,46 @@ __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __
     for (int i = 0; i < WV; ++i)
         dst[i] = w[i];
     p.v_meta[tc] = meta;
+}
+
+template <typename T, int BITS>
+__global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __restrict__ v,
+                                                           int n_src, int src_stride, int t_dst0,
+                                                           size_t total)
+{
+    quant_values_thread<T, BITS>(p, v, n_src, src_stride, t_dst0, total,
+                                 (size_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// Keys and values of a prefill in one launch: the two codecs read disjoint
+// inputs and write disjoint planes, so their blocks interleave (even blocks
+// keys, odd blocks values while both last) and the two streams overlap
+// instead of running one after the other.  Key block kb covers key-group
+// block kb % kgx of sequence/head kb / kgx.
+template <typename T, int KB, int VB>
+__global__ __launch_bounds__(256) void quant_kv_kernel(Planes p, const T* __restrict__ k,
+                                                       int n_tokens, int g_begin, int g_end,
+                                                       int kgx, unsigned kblocks,
+                                                       const T* __restrict__ v, int n_src,
+                                                       int t_dst0, size_t vtotal, unsigned vblocks)
+{
+    const unsigned b = blockIdx.x;
+    const unsigned both = 2u * (kblocks < vblocks ? kblocks : vblocks);
+    bool key;
+    unsigned i;
+    if (b < both) {
+        key = (b & 1u) == 0;
+        i = b >> 1;
+    } else {
+        key = kblocks > vblocks;
+        i = (both >> 1) + (b - both);
+    }
+    if (key)
+        quant_keys_block<T, KB>(p, k, n_tokens, g_begin, g_end, (int)(i % (unsigned)kgx),
+                                i / (unsigned)kgx);
+    else
+        quant_values_thread<T, VB>(p, v, n_src, n_tokens, t_dst0, vtotal,
+                                   (size_t)i * blockDim.x + threadIdx.x);
 }
 
 // Append one token per sequence/head in one launch (block = one sequence/head,
@@ -307,9 +353,39 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
     const int tq = quantized_end(n_tokens, p.residual, p.sink);
     const int g_begin = p.sink / G, g_end = tq / G;
     const int nbh = p.nb * p.hkv;
-    if (g_end > g_begin) {
-        const int gpb = 256 / p.D;
-        dim3 grid((g_end - g_begin + gpb - 1) / gpb, nbh);
+    // values: every token from S on quantized without a window; with one,
+    // [S, tq) quantized and the rest copied to the value ring
+    const int vq = p.residual > 0 ? tq : n_tokens;
+    const int v0 = ns;  // first quantized value token (S, or n_tokens while n_tokens < S)
+    const size_t vg = vq > v0 ? (size_t)nbh * (vq - v0) * (p.D / G) : 0;
+    const unsigned vblocks = (unsigned)((vg + 255) / 256);
+    const T* vsrc = v + (size_t)v0 * p.D;  // token v0 of sequence/head 0; rows of n_tokens
+    const int gpb = 256 / p.D;
+    const int kgx = g_end > g_begin ? (g_end - g_begin + gpb - 1) / gpb : 0;
+    const unsigned kblocks = (unsigned)kgx * (unsigned)nbh;
+    bool values_done = false;
+    if (kblocks > 0 && vblocks > 0 && gpb * p.D == 256) {
+        // both codecs in one launch
+        const unsigned blocks = kblocks + vblocks;
+#define KVQ_KV(KBB, VBB)                                                                     \
+    quant_kv_kernel<T, KBB, VBB><<<blocks, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end, \
+                                                             kgx, kblocks, vsrc, vq - v0, v0,   \
+                                                             vg, vblocks)
+        switch (p.kbits * 16 + p.vbits) {
+        case 2 * 16 + 2: KVQ_KV(2, 2); break;
+        case 2 * 16 + 4: KVQ_KV(2, 4); break;
+        case 2 * 16 + 8: KVQ_KV(2, 8); break;
+        case 4 * 16 + 2: KVQ_KV(4, 2); break;
+        case 4 * 16 + 4: KVQ_KV(4, 4); break;
+        case 4 * 16 + 8: KVQ_KV(4, 8); break;
+        case 8 * 16 + 2: KVQ_KV(8, 2); break;
+        case 8 * 16 + 4: KVQ_KV(8, 4); break;
+        case 8 * 16 + 8: KVQ_KV(8, 8); break;
+        }
+#undef KVQ_KV
+        values_done = true;
+    } else if (kblocks > 0) {
+        dim3 grid(kgx, nbh);
         switch (p.kbits) {
         case 2: quant_keys_kernel<T, 2><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
         case 4: quant_keys_kernel<T, 4><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
@@ -325,16 +401,9 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
     copy(k, p.k_tail, p.ring, tq, n_tokens);
     copy(k, p.k_sink, p.sink, 0, ns);
     copy(v, p.v_sink, p.sink, 0, ns);
-    // values: every token from S on quantized without a window; with one,
-    // [S, tq) quantized and the rest copied to the value ring
-    const int vq = p.residual > 0 ? tq : n_tokens;
     if (p.residual > 0)
         copy(v, p.v_tail, p.ring, tq, n_tokens);
-    const int v0 = ns;  // first quantized value token (S, or n_tokens while n_tokens < S)
-    const size_t vg = vq > v0 ? (size_t)nbh * (vq - v0) * (p.D / G) : 0;
-    const unsigned vblocks = (unsigned)((vg + 255) / 256);
-    const T* vsrc = v + (size_t)v0 * p.D;  // token v0 of sequence/head 0; rows of n_tokens
-    if (vg > 0) {
+    if (vg > 0 && !values_done) {
         switch (p.vbits) {
         case 2: quant_values_kernel<T, 2><<<vblocks, 256, 0, stream>>>(p, vsrc, vq - v0, n_tokens, v0, vg); break;
         case 4: quant_values_kernel<T, 4><<<vblocks, 256, 0, stream>>>(p, vsrc, vq - v0, n_tokens, v0, vg); break;
