@@ -1,5 +1,6 @@
 // kvq_kernels.hip -- gfx950 kernels: key/value quantize-and-pack and the
-// key-tail append and flush (decode attention lives in kvq_attend.hip).
+// key-tail append and flush (decode attention lives in kvq_attend_kernel.h,
+// instantiated by kvq_attend_d64.hip and kvq_attend_d128.hip).
 //
 // Method (web pages): uniform asymmetric integer codes per group, zero point
 // = group minimum, step = range/(2^B-1), nearest step ("Your KV Cache Doesn't
