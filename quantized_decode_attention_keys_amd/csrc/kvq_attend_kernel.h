@@ -375,20 +375,28 @@ __device__ __forceinline__ void softmax_weights(int lane, int t_base, int t_end,
 #pragma unroll
     for (int h = 0; h < QPK; ++h) {
         const float sv = own_valid ? s[h] : -INFINITY;
-        const float m_new = max_nn(st.m[h], wave_max<S::NP == 64>(sv));
-        // arguments <= 0; v_exp_f32 returns 0 for -inf and for results below
-        // the fp32 normal range, which weigh nothing at this tolerance
-        const float alpha = __builtin_amdgcn_exp2f(st.m[h] - m_new);  // 0 on the first step
-        const float pl = own_valid ? __builtin_amdgcn_exp2f(sv - m_new) : 0.f;
-        st.l[h] = st.l[h] * alpha + (counts ? pl : 0.f);
-        st.m[h] = m_new;
-        pw[h] = pl;
-        if (alpha != 1.f) {  // uniform across the wave
-            st.z[h] *= alpha;
+        // Most steps raise no score above the running maximum (one compare
+        // and a ballot tell); only the others reduce the wave's maximum and
+        // rescale.  Either way m_new = max(m, scores), bit for bit.
+        const bool raises = __builtin_amdgcn_ballot_w64(sv > st.m[h]) != 0;  // uniform
+        if (raises) {
+            const float m_new = max_nn(st.m[h], wave_max<S::NP == 64>(sv));
+            // arguments <= 0; v_exp_f32 returns 0 for -inf and for results
+            // below the fp32 normal range, which weigh nothing at this
+            // tolerance
+            const float alpha = __builtin_amdgcn_exp2f(st.m[h] - m_new);  // 0 on the first step
+            st.l[h] *= alpha;
+            st.m[h] = m_new;
+            if (alpha != 1.f) {  // uniform across the wave
+                st.z[h] *= alpha;
 #pragma unroll
-            for (int c = 0; c < S::NCL; ++c)
-                st.o[h][c] *= alpha;
+                for (int c = 0; c < S::NCL; ++c)
+                    st.o[h][c] *= alpha;
+            }
         }
+        const float pl = own_valid ? __builtin_amdgcn_exp2f(sv - st.m[h]) : 0.f;
+        st.l[h] += counts ? pl : 0.f;
+        pw[h] = pl;
     }
 }
 
