@@ -359,6 +359,11 @@ __device__ __forceinline__ void load_keys(
     sd.rg = rope_group[(size_t)gb * S::NP + gl * S::NP + i];
 }
 
+// Whether a step tests for a raised maximum before the wave reduction and
+// rescale (a ballot), rather than always doing both.  Measured faster with
+// 2-bit values or several query heads, slower with one head and 4-bit values.
+constexpr bool skips_rescale(int vb, int qpk) { return qpk > 1 || vb <= 2; }
+
 // Online-softmax update for one wave step.  Lane `lane` holds score s[h] of
 // token tt = lane (head_dim 64) or lane & 31 (head_dim 128), i.e. token
 // t_base + tt; tokens at or past t_end are absent and weigh exactly 0.
@@ -376,9 +381,11 @@ __device__ __forceinline__ void softmax_weights(int lane, int t_base, int t_end,
     for (int h = 0; h < QPK; ++h) {
         const float sv = own_valid ? s[h] : -INFINITY;
         // Most steps raise no score above the running maximum (one compare
-        // and a ballot tell); only the others reduce the wave's maximum and
-        // rescale.  Either way m_new = max(m, scores), bit for bit.
-        const bool raises = __builtin_amdgcn_ballot_w64(sv > st.m[h]) != 0;  // uniform
+        // and a ballot tell); with skips_rescale only the others reduce the
+        // wave's maximum and rescale.  Either way m_new = max(m, scores), bit
+        // for bit.
+        const bool raises = !skips_rescale(VB, QPK) ||
+                            __builtin_amdgcn_ballot_w64(sv > st.m[h]) != 0;  // uniform
         if (raises) {
             const float m_new = max_nn(st.m[h], wave_max<S::NP == 64>(sv));
             // arguments <= 0; v_exp_f32 returns 0 for -inf and for results
