@@ -76,6 +76,36 @@ def test_d64_gqa(bits, qpk):
     _attend_both(cfg, cache, op, gp, n)
 
 
+@pytest.mark.parametrize("bits, qpk", [((2, 2), 1), ((4, 4), 1), ((4, 2), 1), ((2, 2), 4)])
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_scores_monotone_in_position(bits, qpk, direction):
+    """Scores that rise along the sequence (nearly every step raises the
+    running maximum and rescales the accumulators) or fall (only the first
+    step does).  The keys' energy sits in the last channel, which either
+    rotary pairing turns at the lowest frequency (under 0.12 rad over 1000
+    tokens), so q.k follows the key's magnitude there."""
+    cfg = synth.scaled(synth.CONFIGS["llama2_7b"], batch=2, kv_heads=2, q_heads=2 * qpk,
+                       n_tokens=1000, key_bits=bits[0], value_bits=bits[1])
+    n, D = 1000, cfg.head_dim
+    k = synth.make_keys(cfg, 3, 0, n).astype(np.float32) * 0.01
+    ramp = 0.02 * np.arange(n, dtype=np.float32)
+    k[..., D - 1] += ramp if direction == "rising" else ramp[::-1]
+    k = np.ascontiguousarray(k.astype(cfg.np_dtype))
+    v = synth.make_values(cfg, 3, 0, n)
+    cache = make_cache(cfg, 1024)
+    cache.prefill(to_gpu(k), to_gpu(v))
+    gp = gpu_planes(cache)
+    op = oracle_planes(cfg, k, v, 1024)
+    assert_planes_equal(gp, op, n)
+    q = synth.make_query(cfg, 3).astype(np.float32) * 0.01
+    q[..., D - 1] = 4.0
+    q = np.ascontiguousarray(q.astype(cfg.np_dtype))
+    out = cache.attend(to_gpu(q)).cpu().numpy()
+    for planes in (op, gp):
+        ref = oracle.attend(planes, q, n, cfg.key_bits, cfg.value_bits, cfg.kv_heads)
+        assert_attention_close(out, ref)
+
+
 def test_append_through_tail_and_flushes():
     """Prefill 250 tokens, append 40 one at a time (flushes at n = 256 and
     288); planes equal the oracle's one-shot quantization of all tokens and
