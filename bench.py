@@ -16,9 +16,17 @@ in that cache when its step starts: the bytes come from HBM.
 
 Prints one JSON line.  value = decode-attention algorithmic bytes moved per
 second over the timed steps (wall clock, launches included); the roofline
-object reports the attention kernel alone, timed with HIP events on the
-stream it runs on, over as many further steps (events in the timed steps
-would add their own queue packets to the wall clock).
+object reports the attention kernel alone against the HBM roofline, timed
+with HIP events on the stream it runs on, over as many further steps (events
+in the timed steps would add their own queue packets to the wall clock),
+with the VALU view beside it.  A third set of event-timed steps writes a
+1 GiB scratch buffer before each step (flushing the Infinity Cache), so each
+line also shows whether cache residency inflates the rotating-cache figure.
+
+--decode-loop K (with --config llama2_13b or llama2_13b_b4): prefill the
+prompt once, then time K consecutive decode steps on that one cache end to
+end (appends included, no flush inside the loop); prints tokens/s = batch *
+K / loop time instead.
 """
 from __future__ import annotations
 
@@ -33,9 +41,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, vendor figure
 FP32_UNPACKED_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12  # 78.6: one FMA per lane per cycle
 INFINITY_CACHE = 256 << 20  # bytes
+FLUSH_BYTES = 1 << 30       # scratch written before each flushed step
+SIMDS = 256 * 4             # compute units x SIMDs per CU
+NOMINAL_CLOCK_HZ = 2.4e9    # MI355X peak engine clock
 KERNEL_SOURCES = ["quantized_decode_attention_keys_amd/csrc/kvq_attend_kernel.h",
                   "quantized_decode_attention_keys_amd/csrc/kvq_append.h",
                   "quantized_decode_attention_keys_amd/csrc/kvq_internal.h"]
@@ -51,18 +61,31 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(config_name: str):
-    """HBM bytes per attention launch from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or None when there is none for this
-    workload or the kernel source changed since it was taken."""
+def measured_counters(config_name: str):
+    """The committed rocprofv3 counter record of the attention kernel for
+    this workload (HBM bytes per launch from FETCH_SIZE/WRITE_SIZE, VALU
+    instructions per launch from SQ_INSTS_VALU), or {} when there is none or
+    the kernel source changed since it was taken."""
     path = os.path.join(ROOT, TRAFFIC_FILE)
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("config") != config_name:
-        return None
-    return rec.get("bytes_per_launch")
+        return {}
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def calibrate_copy():
@@ -248,8 +271,94 @@ def cpu_baseline(cfg, n: int, budget_s: float = 12.0, residual: int = 0, sink: i
         "sample": f"decode attention of {rows_done} of {cfg.batch * cfg.q_heads} (sequence, head) "
                   f"rows at n={n}, {t_total:.1f} s on one host core "
                   f"(host has {os.cpu_count()} cores); same algorithmic bytes per row as the GPU",
+        "cpu_model": cpu_model(),
         "tokens_per_s": round(rows_done / cfg.q_heads / t_total, 4),
     }
+
+
+def decode_loop(cfg, steps: int, dev):
+    """K consecutive decode steps on one cache, timed end to end: prefill
+    the n-token prompt, then per step append the next token and attend with
+    that step's query (one kvq_append_attend call), no flush inside the loop.
+    The code objects are loaded first on a one-group cache of the same
+    shape, so the loop's first step does not pay for it."""
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_decode_attention_keys_amd import QuantizedKVCache
+    from quantized_decode_attention_keys_amd import _lib as L
+
+    n0 = cfg.n_tokens
+    tdt = torch.float16 if cfg.dtype == "float16" else torch.float32
+    cap = n0 + steps
+    k_new = torch.from_numpy(synth.make_keys(cfg, 0, n0, cap)).to(dev)
+    v_new = torch.from_numpy(synth.make_values(cfg, 0, n0, cap)).to(dev)
+    k_new = [k_new[:, :, i].contiguous() for i in range(steps)]
+    v_new = [v_new[:, :, i].contiguous() for i in range(steps)]
+    qs = [torch.from_numpy(synth.make_query(cfg, 0, s + 1)).to(dev) for s in range(steps)]
+    out = torch.empty((cfg.batch, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+
+    def new_cache(cap_tokens):
+        return QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cap_tokens,
+                                cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev)
+
+    warm = new_cache(2 * cfg.group)
+    k = torch.from_numpy(synth.make_keys(cfg, 0, 0, cfg.group)).to(dev)
+    v = torch.from_numpy(synth.make_values(cfg, 0, 0, cfg.group)).to(dev)
+    warm.prefill(k, v)
+    for i in range(3):
+        warm.append_attend(k_new[i], v_new[i], qs[i], out)
+    torch.cuda.synchronize()
+    warm.close()
+
+    loops = []
+    lib = L.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for rep in range(2):  # two loops, each on a freshly prefilled cache
+        cache = new_cache(cap)
+        k = torch.from_numpy(synth.make_keys(cfg, 0, 0, n0)).to(dev)
+        v = torch.from_numpy(synth.make_values(cfg, 0, 0, n0)).to(dev)
+        cache.prefill(k, v)
+        del k, v
+        torch.cuda.synchronize()
+        h = cache.handle
+        args = [(k_new[i].data_ptr(), v_new[i].data_ptr(), qs[i].data_ptr()) for i in range(steps)]
+        op = out.data_ptr()
+        status = 0
+        t0 = time.perf_counter()
+        for kp, vp, qp in args:
+            status |= lib.kvq_append_attend(h, kp, vp, qp, op, stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if status != 0 or len(cache) != cap:
+            raise RuntimeError("a library call failed during the decode loop")
+        loops.append(t1 - t0)
+        cache.close()
+        print(f"decode loop {rep}: {steps} steps in {(t1 - t0) * 1e3:.3f} ms", file=sys.stderr,
+              flush=True)
+    best = min(loops)
+    total_bytes = sum(attend_bytes(cfg, n0 + s + 1) for s in range(steps))
+    res = {
+        "metric": f"{cfg.name} {steps}-step decode loop tokens/s",
+        "value": round(cfg.batch * steps / best, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "loop_ms": [round(t * 1e3, 4) for t in loops],
+        "ms_per_step": round(best / steps * 1e3, 5),
+        "higher_is_better": True,
+        "effective_GB_per_s": round(total_bytes / best / 1e9, 2),
+        "pct_hbm_peak": round(100.0 * total_bytes / best / 1e9 / HBM_PEAK_GBS, 2),
+        "dtype": "f32 (value weights p*step in binary16)",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "batch": cfg.batch,
+                   "q_heads": cfg.q_heads, "kv_heads": cfg.kv_heads,
+                   "head_dim": cfg.head_dim, "prompt": n0, "key_bits": cfg.key_bits,
+                   "value_bits": cfg.value_bits, "step_calls": "kvq_append_attend",
+                   "context_during_steps": [n0 + 1, n0 + steps]},
+    }
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -276,6 +385,12 @@ def main():
                     help="skip the error-where-consumed metrics of the prompt cache")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the traffic counters)")
+    ap.add_argument("--flush-mode", default="read", choices=["read", "write", "rw"],
+                    help="how the flushed steps clear the Infinity Cache: read, write, or read "
+                         "and write a 1 GiB scratch buffer before each step")
+    ap.add_argument("--decode-loop", type=int, default=0, metavar="K",
+                    help="time K consecutive decode steps on one cache end to end "
+                         "(tokens/s = batch * K / loop time) instead of the rotating-cache steps")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -297,6 +412,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cfg = synth.CONFIGS[args.config]
+    if args.decode_loop > 0:
+        decode_loop(cfg, args.decode_loop, dev)
+        return
     fp8 = args.format == "fp8"
     if fp8:
         cfg = synth.scaled(cfg, key_bits=8, value_bits=8,
@@ -305,8 +423,9 @@ def main():
     tdt = torch.float16 if cfg.dtype == "float16" else torch.float32
     # warm-up, the timed steps, then as many again with HIP events around
     # each launch (the per-launch figures): events add queue packets and
-    # host calls, so the timed steps carry none
-    total_steps = args.warmup + 2 * args.steps
+    # host calls, so the timed steps carry none; then as many again with a
+    # 1 GiB scratch write before each (Infinity Cache flushed)
+    total_steps = args.warmup + 3 * args.steps
 
     Rw, Sw = args.residual, args.sink
     geom = GEOMETRIES[args.geometry]
@@ -371,7 +490,17 @@ def main():
     append, attend = lib.kvq_append_token, lib.kvq_attend_decode
     append_attend = lib.kvq_append_attend
 
-    hev = HipEvents(2 * args.steps)
+    hev = HipEvents(4 * args.steps)
+    scratch = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        if args.flush_mode == "read":  # clean lines only: nothing to write back later
+            torch.sum(scratch, out=flush_sink)
+        elif args.flush_mode == "write":
+            scratch.fill_(0.0)
+        else:
+            scratch.add_(1.0)
     record = hev.hip.hipEventRecord
     evp = hev.ev
 
@@ -418,6 +547,12 @@ def main():
     for j in range(args.steps):
         status |= step(ev_base + j, j)
     torch.cuda.synchronize()
+    fl_base = ev_base + args.steps
+    fl_lengths = [n - 1 + (fl_base + j) // R + 1 for j in range(args.steps)]
+    for j in range(args.steps):
+        flush()  # 1 GiB through the caches on the same stream: the step starts cold
+        status |= step(fl_base + j, args.steps + j)
+    torch.cuda.synchronize()
     if status != 0:
         raise RuntimeError(f"a library call failed during the timed steps (status bits {status})")
     if [len(c) for c in caches] != [n - 1 + len(range(r, total_steps, R)) for r in range(R)]:
@@ -427,12 +562,20 @@ def main():
     total_bytes = sum(step_bytes(L) for L in lengths)
     value = total_bytes / wall / 1e9
     attend_ms = np.array([hev.elapsed_ms(2 * j, 2 * j + 1) for j in range(args.steps)])
+    flushed_ms = np.array([hev.elapsed_ms(2 * j, 2 * j + 1)
+                           for j in range(args.steps, 2 * args.steps)])
     hev.close()
+    del scratch
     att_avg_s = float(attend_ms.mean()) / 1e3
     bytes_per_launch = sum(step_bytes(L) for L in ev_lengths) / len(ev_lengths)
     achieved = bytes_per_launch / att_avg_s / 1e9
     flops_per_launch = sum(attend_flops(cfg, L) for L in ev_lengths) / len(ev_lengths)
     achieved_tflops = flops_per_launch / att_avg_s / 1e12
+    fl_avg_s = float(flushed_ms.mean()) / 1e3
+    fl_bytes = sum(step_bytes(L) for L in fl_lengths) / len(fl_lengths)
+    counters = (measured_counters(cfg.name) if Rw == 0 and Sw == 0 and geom == 0 and not fp8
+                else {})
+    valu_insts = counters.get("sq_insts_valu_per_launch")
 
     res = {
         "metric": "quantized decode-attention effective KV GB/s (% of HBM peak); tokens/s",
@@ -445,7 +588,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # scores, softmax and accumulators in fp32; the value side multiplies
+        # each code by its weight p*step rounded to binary16 (integer cache)
+        "dtype": "f32" if fp8 or geom else "f32 (value weights p*step in binary16)",
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {cfg.description}",
@@ -465,13 +610,14 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(cfg.batch * args.steps / wall, 1),
         "roofline": {
-            "bound": "alu",
-            "achieved": round(achieved_tflops, 3),
-            "peak": FP32_VECTOR_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
-            "traffic": (measured_traffic(cfg.name) if Rw == 0 and Sw == 0 and geom == 0
-                        and not fp8 else None),
+            # the attention kernel against the HBM roofline: algorithmic
+            # bytes per launch / mean event-timed launch duration
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": counters.get("bytes_per_launch"),
             "kernel": ("attend_fp8_kernel (FP8 E4M3 decode attention)" if fp8 else
                        "attend_kernel (decode attention)" if geom == 0 else
                        "attend_geometry_kernel (geometry ablation attention)")
@@ -481,18 +627,28 @@ def main():
                          "; HIP events around each kvq_append_attend call (append and attention"
                          " in one launch for a plain cache), over as many steps after the"
                          " timed ones"),
-            "flops_per_launch": int(flops_per_launch),
             "bytes_per_launch": int(bytes_per_launch),
             "avg_launch_us": round(att_avg_s * 1e6, 3),
             "p10_p90_us": [round(float(np.percentile(attend_ms, 10)) * 1e3, 3),
                            round(float(np.percentile(attend_ms, 90)) * 1e3, 3)],
-            "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4)},
-            # the fp32 vector peak above counts packed FMAs (two per lane per
-            # cycle); code built without packed fp32 issues one per lane per
-            # cycle: 256 CUs x 64 lanes x 2 flops x 2.4 GHz
-            "fp32_unpacked": {"peak": FP32_UNPACKED_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": round(achieved_tflops / FP32_UNPACKED_PEAK_TFLOPS, 4)},
+            # the same launches with the Infinity Cache flushed before each
+            "flushed": {"mode": args.flush_mode,
+                        "avg_launch_us": round(fl_avg_s * 1e6, 3),
+                        "achieved": round(fl_bytes / fl_avg_s / 1e9, 2),
+                        "frac": round(fl_bytes / fl_avg_s / 1e9 / HBM_PEAK_GBS, 4)},
+            # the VALU view: the method's fp32 arithmetic against the one-FMA-
+            # per-lane rate (the library is built without packed fp32), and
+            # the VALU instruction issue the counters measured
+            "valu": {
+                "flops_per_launch": int(flops_per_launch),
+                "achieved": round(achieved_tflops, 3),
+                "peak": round(FP32_UNPACKED_PEAK_TFLOPS, 1),
+                "unit": "TFLOP/s",
+                "frac": round(achieved_tflops / FP32_UNPACKED_PEAK_TFLOPS, 4),
+                "insts_per_launch": valu_insts,
+                "issue_frac_at_2.4GHz": (round(valu_insts * 4 / SIMDS / NOMINAL_CLOCK_HZ
+                                               / att_avg_s, 4) if valu_insts else None),
+            },
         },
         "prefill": {
             "tokens": n - 1,

@@ -69,8 +69,9 @@
  * R = 0 every value is quantized on arrival and only the < G keys of the
  * unfilled group wait).  With R > 0 at least R and at most R + G - 1 recent
  * tokens are unquantized; a G-block is quantized when it leaves the window.
- * Sink window S = kvq_config.sink (same page and section: InnerQ keeps the
- * first tokens in high precision): keys and values of tokens [0, min(n, S))
+ * Sink window S = kvq_config.sink (same page, section "Where the Work Is
+ * Headed": InnerQ keeps high-precision windows for the recent tokens and the
+ * attention-sink tokens): keys and values of tokens [0, min(n, S))
  * stay unquantized for good, quantization starts at token S, and Tq above is
  * raised to at least min(n, S).
  * Geometry ablation, kvq_config.geometry (the page "Your KV Cache Doesn't Have

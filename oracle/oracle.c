@@ -37,8 +37,8 @@
  *      at least R (at most R + G - 1) recent tokens; a G-block is quantized
  *      when it leaves the window.  R = 0: Tq = G * floor(n / G) for keys and
  *      every value is quantized on arrival.
- *      Sink window S (InnerQ keeps the first tokens in high precision;
- *      [BITS], same section): keys and values of tokens [0, min(n, S)) stay
+ *      Sink window S (InnerQ keeps high-precision windows for recent and
+ *      attention-sink tokens; [BITS, "Where the Work Is Headed"]): keys and values of tokens [0, min(n, S)) stay
  *      unquantized for good; the quantized region starts at S (a multiple of
  *      G, so key groups stay aligned to token 0) and Tq is raised to at
  *      least min(n, S).

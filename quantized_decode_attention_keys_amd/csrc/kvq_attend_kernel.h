@@ -937,7 +937,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     // beside the other waves' groups, paced by the priorities, instead of
     // alone after them; a wave's first group is loaded after them either
     // way, so no group's words are held in registers across the chunk code.
-    if constexpr (chunks_first(KB, VB, QPK)) {
+    auto score_chunks = [&]() __attribute__((always_inline)) {
         for (int ch = chunk0; ch < nchunks; ch += nwaves) {
             asm volatile("" : "+v"(tw_base));  // keep the twiddle reads in the loop
             set_priority();
@@ -954,7 +954,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
             const size_t trow = row0 * D + 2 * i;  // element index of (token t0, channel 2i)
             if (p.dtype == 0) {
                 const uint32_t* t32 = reinterpret_cast<const uint32_t*>(krows) + trow / 2;
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < G; ++j) {
                     const uint32_t w = (gsub == 0 && j < cnt) ? t32[(size_t)j * (D / 2)] : 0u;
                     tx[j] = lo_h(w);
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 }
             } else {
                 const float2* t64 = reinterpret_cast<const float2*>(krows) + trow / 2;
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < G; ++j) {
                     const float2 w = (gsub == 0 && j < cnt) ? t64[(size_t)j * (D / 2)]
                                                             : make_float2(0.f, 0.f);
@@ -972,10 +972,10 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
             }
             const float2 rg = p.rope_group[(size_t)(t0 / G) * NP + i];
             float s[QPK];
-    #pragma unroll
+#pragma unroll
             for (int h = 0; h < QPK; ++h) {
                 const float2 Q = cmul(qc[h], rg);
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < G; ++j) {
                     // Re[T_j Q (x + iy)]; the twiddle carries (T.x, -T.y) * 2^(24-pos)
                     const float vr = Q.x * tx[j] - Q.y * ty[j];
@@ -985,7 +985,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                     red[lane * RS + j] = fmaf(tw.x, vr, tw.y * vi) * unscale;
                 }
                 float a4[4] = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                 for (int m = 0; m < 32; ++m)
                     a4[m & 3] += red[(red_half + m) * RS + red_col];
                 float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
@@ -1003,7 +1003,9 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 softmax_values<D, KB, VB, QPK>(lane, t0, n, s, vw, vm, st);
             }
         }
-    }
+    };
+    if constexpr (chunks_first(KB, VB, QPK))
+        score_chunks();
     if (gb < g1) {
         load_keys<D, KB, VB, QPK>(hp, p.rope_group, lane, gb, g1, cur);
         if constexpr (!kDefer)
@@ -1022,73 +1024,8 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     if (kDefer && has_prev)
         accumulate_values<D, KB, VB, QPK>(lane, pw_prev, last_in_nxt ? nxt.vw : cur.vw,
                                           last_in_nxt ? nxt.vm : cur.vm, st);
-    if constexpr (!chunks_first(KB, VB, QPK)) {  // the same chunks, after the groups
-        for (int ch = chunk0; ch < nchunks; ch += nwaves) {
-            asm volatile("" : "+v"(tw_base));  // keep the twiddle reads in the loop
-            set_priority();
-            // One chunk of unquantized tokens t0 .. t0+cnt-1, from the sinks or
-            // the rings (rows from row0, contiguous: the ring and t0 are
-            // multiples of G), scored like one more group (the softmax is
-            // order-free): lane = channel pair, the tokens across its registers.
-            const bool in_sink = ch < nsink_chunks;
-            const int t0 = in_sink ? ch * G : tq + (ch - nsink_chunks) * G;
-            const int cnt = min(G, (in_sink ? ns : n) - t0);
-            const size_t row0 = in_sink ? bh * (size_t)p.sink + t0 : bh * (size_t)p.ring + t0 % p.ring;
-            const void* const krows = in_sink ? p.k_sink : p.k_tail;
-            float tx[G], ty[G];
-            const size_t trow = row0 * D + 2 * i;  // element index of (token t0, channel 2i)
-            if (p.dtype == 0) {
-                const uint32_t* t32 = reinterpret_cast<const uint32_t*>(krows) + trow / 2;
-    #pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    const uint32_t w = (gsub == 0 && j < cnt) ? t32[(size_t)j * (D / 2)] : 0u;
-                    tx[j] = lo_h(w);
-                    ty[j] = hi_h(w);
-                }
-            } else {
-                const float2* t64 = reinterpret_cast<const float2*>(krows) + trow / 2;
-    #pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    const float2 w = (gsub == 0 && j < cnt) ? t64[(size_t)j * (D / 2)]
-                                                            : make_float2(0.f, 0.f);
-                    tx[j] = w.x;
-                    ty[j] = w.y;
-                }
-            }
-            const float2 rg = p.rope_group[(size_t)(t0 / G) * NP + i];
-            float s[QPK];
-    #pragma unroll
-            for (int h = 0; h < QPK; ++h) {
-                const float2 Q = cmul(qc[h], rg);
-    #pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    // Re[T_j Q (x + iy)]; the twiddle carries (T.x, -T.y) * 2^(24-pos)
-                    const float vr = Q.x * tx[j] - Q.y * ty[j];
-                    const float vi = Q.x * ty[j] + Q.y * tx[j];
-                    const float unscale = 1.0f / (float)(1 << (24 - KC::pos(j % KC::TPH)));
-                    const float2 tw = twiddle(j);
-                    red[lane * RS + j] = fmaf(tw.x, vr, tw.y * vi) * unscale;
-                }
-                float a4[4] = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
-                for (int m = 0; m < 32; ++m)
-                    a4[m & 3] += red[(red_half + m) * RS + red_col];
-                float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-                if (NP == 64)
-                    acc = half_sum(acc);
-                s[h] = acc;
-            }
-            if (in_sink || p.residual > 0) {
-                const char* vrows = static_cast<const char*>(in_sink ? p.v_sink : p.v_tail) +
-                                    row0 * D * (p.dtype == 0 ? 2 : 4);
-                softmax_fp_values<D, KB, VB, QPK>(lane, t0, cnt, s, vrows, p.dtype, st);
-            } else {
-                uint32_t vw[S::NVW], vm[S::NVM];
-                load_values<D, KB, VB, QPK, true>(hp, lane, t0, n - 1, vw, vm);
-                softmax_values<D, KB, VB, QPK>(lane, t0, n, s, vw, vm, st);
-            }
-        }
-    }
+    if constexpr (!chunks_first(KB, VB, QPK))  // the same chunks, after the groups
+        score_chunks();
 
     __builtin_amdgcn_s_setprio(0);
 

@@ -39,8 +39,10 @@ struct Planes {
     int format;          // 0: integer codes; kFormatFp8: E4M3 bytes in k_codes/v_codes
 };
 
-// FP8 (E4M3) cache: one byte per element, channel-major in 32-token groups,
-// [nb][hkv][gcap][D][32] inside the k_codes and v_codes planes.
+// FP8 (E4M3) cache: one byte per element inside the k_codes and v_codes
+// planes, a D*32-byte block per (sequence, head, 32-token group) made of
+// 16-byte pieces: channel c of token j at byte
+// ((2*(c%2) + j/16) * D/2 + c/2) * 16 + j%16 of its block (fp8_offset).
 constexpr int kFormatFp8 = 1;
 
 // Geometry ablation bits: keys grouped like values (G channels of one token,

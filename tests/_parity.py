@@ -8,6 +8,7 @@ import synth
 from quantized_decode_attention_keys_amd import QuantizedKVCache
 
 TOL = 2e-3  # attention: max|out - ref| <= TOL * max|ref| over the output tensor
+G = 32
 
 _TORCH = {np.dtype(np.float16): torch.float16, np.dtype(np.float32): torch.float32}
 
@@ -20,10 +21,11 @@ def to_gpu(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
 
 
-def make_cache(cfg, max_tokens, residual=0, sink=0):
+def make_cache(cfg, max_tokens, residual=0, sink=0, geometry=0):
     return QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, max_tokens,
                             cfg.key_bits, cfg.value_bits, _TORCH[cfg.np_dtype],
-                            rope_base=cfg.rope_base, device=dev(), residual=residual, sink=sink)
+                            rope_base=cfg.rope_base, device=dev(), residual=residual, sink=sink,
+                            geometry=geometry)
 
 
 def gpu_planes(cache):
@@ -74,6 +76,25 @@ def assert_planes_equal(gp, op, n, G=32, seqs=None, residual=0, sink=0):
     for name in (("k_sink", "v_sink") if sink > 0 else ()):
         at, bt = g[name][:, :, :ns], o[name][:, :, :ns]
         assert np.array_equal(at.view(np.uint8), bt.view(np.uint8)), f"{name} differs"
+
+
+def assert_geometry_planes_equal(gp, op, n, geom, seqs=None):
+    sel = slice(None) if seqs is None else list(seqs)
+    tq = n // G * G
+    for op_name, per_token in (("k", bool(geom & 1)), ("v", not geom & 2)):
+        for part in ("codes", "meta"):
+            name = f"{op_name}_{part}"
+            hi = n if per_token else tq // G
+            a, b = gp[name][sel][:, :, :hi], op[name][:, :, :hi]
+            if not np.array_equal(a, b):
+                bad = np.argwhere(a != b)
+                raise AssertionError(f"geometry {geom} {name}: {len(bad)} mismatches, first "
+                                     f"at {bad[0].tolist()}")
+        if not per_token:
+            slots = [t % G for t in range(tq, n)]
+            a = gp[f"{op_name}_tail"][sel][:, :, slots]
+            b = op[f"{op_name}_tail"][:, :, slots]
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{op_name}_tail"
 
 
 def assert_attention_close(out, ref, tol=TOL):

@@ -44,8 +44,7 @@ def test_llama2_13b_decode_loop():
     cache.prefill(to_gpu(synth.make_keys(cfg, 0, 0, n0)), to_gpu(synth.make_values(cfg, 0, 0, n0)))
     k_new = to_gpu(synth.make_keys(cfg, 0, n0, cap))
     v_new = to_gpu(synth.make_values(cfg, 0, n0, cap))
-    sample = 3
-    planes_at = {}
+    seqs = (3, 12)
     outs = {}
     for s in range(1, steps + 1):
         q = synth.make_query(cfg, 0, s)
@@ -56,13 +55,14 @@ def test_llama2_13b_decode_loop():
     torch.cuda.synchronize()
     assert len(cache) == cap
     gp = gpu_planes(cache)
-    for b in (sample, 12):
+    for b in seqs:
         op = _oracle_seq_planes(cfg, b, cap, cap)
         assert_planes_equal(gp, op, cap, seqs=[b])
+    # whole sequences (all 40 heads) at steps around both flushes
     for s, (q, out) in outs.items():
         n = n0 + s
-        planes_at[s] = _oracle_seq_planes(cfg, sample, n, cap)
-        _check_rows(cfg, out, q, planes_at[s], sample, n, heads=range(0, 40, 3))
+        for b in seqs:
+            _check_rows(cfg, out, q, _oracle_seq_planes(cfg, b, n, cap), b, n)
 
 
 def test_llama2_13b_b4_sampled():
@@ -79,13 +79,13 @@ def test_llama2_13b_b4_sampled():
     b = 9
     op = _oracle_seq_planes(cfg, b, n, n)
     assert_planes_equal(gp, op, n, seqs=[b])
-    _check_rows(cfg, out, q, op, b, n, heads=range(0, 40, 4))
+    _check_rows(cfg, out, q, op, b, n)
 
 
 def test_long_context_sampled():
     """131071-token prompt plus one decode step (n = 131072, keys at 4
     bits, values at 2), split over many blocks (the last one appends) and
-    merged by the combine kernel."""
+    merged by the combine kernel; all 32 heads checked."""
     cfg = synth.CONFIGS["long"]
     n = cfg.n_tokens
     cache = make_cache(cfg, n)
@@ -98,7 +98,7 @@ def test_long_context_sampled():
     gp = gpu_planes(cache)
     op = _oracle_seq_planes(cfg, 0, n, n)
     assert_planes_equal(gp, op, n)
-    _check_rows(cfg, out, q, op, 0, n, heads=(0, 13, 31))
+    _check_rows(cfg, out, q, op, 0, n)
 
 
 def test_long_context_ragged_tail():
@@ -115,7 +115,8 @@ def test_long_context_ragged_tail():
 
 
 def test_gqa_sampled():
-    """64 sequences, 32 query heads over 8 KV heads, 16384 tokens."""
+    """64 sequences, 32 query heads over 8 KV heads, 16384 tokens: planes and
+    all 32 heads of four sequences."""
     cfg = synth.CONFIGS["gqa"]
     n = cfg.n_tokens
     cache = make_cache(cfg, n)
@@ -126,7 +127,7 @@ def test_gqa_sampled():
                               to_gpu(synth.make_values(cfg, 0, n - 1, n)[:, :, 0]),
                               to_gpu(q)).cpu().numpy()
     gp = gpu_planes(cache)
-    b = 41
-    op = _oracle_seq_planes(cfg, b, n, n)
-    assert_planes_equal(gp, op, n, seqs=[b])
-    _check_rows(cfg, out, q, op, b, n, heads=range(0, 32, 3))
+    for b in (0, 17, 41, 63):
+        op = _oracle_seq_planes(cfg, b, n, n)
+        assert_planes_equal(gp, op, n, seqs=[b])
+        _check_rows(cfg, out, q, op, b, n)

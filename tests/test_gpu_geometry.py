@@ -9,8 +9,8 @@ import torch
 
 import oracle
 import synth
-from _parity import (TOL, _TORCH, assert_attention_close, assert_planes_equal, dev, gpu_planes,
-                     oracle_planes, to_gpu)
+from _parity import (TOL, _TORCH, assert_attention_close, assert_geometry_planes_equal,
+                     assert_planes_equal, dev, gpu_planes, oracle_planes, to_gpu)
 from quantized_decode_attention_keys_amd import QuantizedKVCache
 
 pytestmark = pytest.mark.gpu
@@ -23,25 +23,6 @@ def make_cache(cfg, cap, geometry=0, residual=0, sink=0):
                             cfg.key_bits, cfg.value_bits, _TORCH[cfg.np_dtype],
                             rope_base=cfg.rope_base, device=dev(), residual=residual, sink=sink,
                             geometry=geometry)
-
-
-def assert_geometry_planes_equal(gp, op, n, geom, seqs=None):
-    sel = slice(None) if seqs is None else list(seqs)
-    tq = n // G * G
-    for op_name, per_token in (("k", bool(geom & 1)), ("v", not geom & 2)):
-        for part in ("codes", "meta"):
-            name = f"{op_name}_{part}"
-            hi = n if per_token else tq // G
-            a, b = gp[name][sel][:, :, :hi], op[name][:, :, :hi]
-            if not np.array_equal(a, b):
-                bad = np.argwhere(a != b)
-                raise AssertionError(f"geometry {geom} {name}: {len(bad)} mismatches, first "
-                                     f"at {bad[0].tolist()}")
-        if not per_token:
-            slots = [t % G for t in range(tq, n)]
-            a = gp[f"{op_name}_tail"][sel][:, :, slots]
-            b = op[f"{op_name}_tail"][:, :, slots]
-            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{op_name}_tail"
 
 
 def check(cfg, cache, k, v, n, geom, cap, q_step=0):

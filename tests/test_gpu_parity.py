@@ -168,20 +168,21 @@ def test_state_and_capacity_errors_leave_state_unchanged():
     torch.cuda.synchronize()
 
 
-def test_llama2_7b_full_size_sampled():
+def test_llama2_7b_full_size():
     """The bench workload at full size (batch 8, 32 heads, 4096 tokens, B=2)
-    in the bench's launch configuration: every plane of sequence 5 bit-exact,
-    and attention for all 32 heads of sequences 0 and 5."""
+    in the bench's launch configuration (the last token appended and
+    attended in one launch): every plane of all 8 sequences bit-exact, and
+    attention for all 256 (sequence, head) rows."""
     cfg = synth.CONFIGS["llama2_7b"]
     n = cfg.n_tokens
     cache, k, v = run_prefill(cfg, n - 1, max_tokens=n + 64)
+    del k, v
     kg = to_gpu(synth.make_keys(cfg, 0, n - 1, n)[:, :, 0])
     vg = to_gpu(synth.make_values(cfg, 0, n - 1, n)[:, :, 0])
-    cache.append(kg, vg)
     q = synth.make_query(cfg, 0, 0)
-    out = cache.attend(to_gpu(q)).cpu().numpy()
+    out = cache.append_attend(kg, vg, to_gpu(q)).cpu().numpy()
     gp = gpu_planes(cache)
-    for b in (0, 5):
+    for b in range(cfg.batch):
         kb = synth.make_keys(cfg, 0, 0, n, seqs=[b])
         vb = synth.make_values(cfg, 0, 0, n, seqs=[b])
         op = oracle_planes(synth.scaled(cfg, batch=1), kb, vb, n + 64)

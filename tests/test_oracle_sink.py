@@ -1,6 +1,6 @@
-"""Pins for the oracle's sink window (InnerQ keeps the first tokens in high
-precision: "Your KV Cache Doesn't Have a Bit Problem...", section "The
-Systems Tax, and Why It Is Not a Detail").
+"""Pins for the oracle's sink window (InnerQ keeps high-precision windows
+for the recent tokens and for the attention-sink tokens: "Your KV Cache
+Doesn't Have a Bit Problem...", section "Where the Work Is Headed").
 
 Reading: with a sink S (a multiple of G), keys and values of tokens
 [0, min(n, S)) stay unquantized for good; quantization starts at token S, so
