@@ -496,7 +496,7 @@ def main():
 
     def flush():
         if args.flush_mode == "read":  # clean lines only: nothing to write back later
-            torch.sum(scratch, out=flush_sink)
+            torch.sum(scratch, dim=0, out=flush_sink)
         elif args.flush_mode == "write":
             scratch.fill_(0.0)
         else:
