@@ -128,8 +128,13 @@ enum {
     KVQ_ERR_STATE = -4,       /* prefill on a non-empty cache, attend on an
                                  empty one                                  */
     KVQ_ERR_CAPACITY = -5,    /* the call would exceed max_tokens           */
-    KVQ_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+    KVQ_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
+    KVQ_ERR_SCRATCH = -7      /* the call needs more than the library's
+                                 static device scratch (KVQ_STATIC_SCRATCH_BYTES) */
 };
+
+/* Bytes of the library's static device scratch (kvq_append_attend_static). */
+#define KVQ_STATIC_SCRATCH_BYTES (4u << 20)
 
 enum { KVQ_F16 = 0, KVQ_F32 = 1 };
 
@@ -256,6 +261,24 @@ int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream);
  * KVQ_ERR_HIP from the attention leaves the append done (n = n + 1). */
 int kvq_append_attend(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
                       float* d_out, void* stream);
+
+/* kvq_append_attend for callers that cannot allocate device memory or touch
+ * the workspace's scratch region while the call runs (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * step with the same arguments, kernels, launch shape, results and state
+ * change, except that the decode attention's split partials live in the
+ * library's own static device array of KVQ_STATIC_SCRATCH_BYTES (4 MiB) per
+ * GPU instead of the workspace's partials region.  The call allocates
+ * nothing.  A step that splits the token range S > 1 ways needs
+ * batch * q_heads * S * (head_dim + 2) * 4 bytes of it; one that does not
+ * split needs none.  The array is found at kvq_create (once per device, with
+ * that device current) and kept until the process ends; it keeps the last
+ * call's contents, and every call on one GPU shares it, so calls that
+ * overlap on one GPU (several streams, several threads) race.
+ * Errors: as kvq_append_attend, and KVQ_ERR_SCRATCH when the step would need
+ * more than the array holds (nothing enqueued, n unchanged). */
+int kvq_append_attend_static(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
+                             float* d_out, void* stream);
 
 /* Error where it is consumed (the page "Your KV Cache Doesn't Have a Bit
  * Problem...", sections "Keys: The Outliers Live in Fixed Channels" and

@@ -16,6 +16,9 @@ KVQ_ERR_WORKSPACE = -3
 KVQ_ERR_STATE = -4
 KVQ_ERR_CAPACITY = -5
 KVQ_ERR_HIP = -6
+KVQ_ERR_SCRATCH = -7
+
+KVQ_STATIC_SCRATCH_BYTES = 4 << 20
 
 KVQ_F16 = 0
 KVQ_F32 = 1
@@ -115,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_attend_decode.restype = ctypes.c_int
         L.kvq_append_attend.argtypes = [P, P, P, P, P, P]
         L.kvq_append_attend.restype = ctypes.c_int
+        L.kvq_append_attend_static.argtypes = [P, P, P, P, P, P]
+        L.kvq_append_attend_static.restype = ctypes.c_int
         L.kvq_error_metrics.argtypes = [P, P, P, P, P, P]
         L.kvq_error_metrics.restype = ctypes.c_int
         L.kvq_destroy.argtypes = [P]
@@ -167,6 +172,11 @@ def kvq_attend_decode(h: int, d_q: int, d_out: int, stream: int) -> int:
 
 def kvq_append_attend(h: int, d_k: int, d_v: int, d_q: int, d_out: int, stream: int) -> int:
     return lib().kvq_append_attend(h, d_k, d_v, d_q, d_out, stream)
+
+
+def kvq_append_attend_static(h: int, d_k: int, d_v: int, d_q: int, d_out: int,
+                             stream: int) -> int:
+    return lib().kvq_append_attend_static(h, d_k, d_v, d_q, d_out, stream)
 
 
 def kvq_error_metrics(h: int, d_k: int, d_v: int, d_q: int, d_metrics: int,

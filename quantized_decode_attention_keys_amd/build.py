@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
 SOURCES = ["kvq_host.cpp", "kvq_kernels.hip", "kvq_attend_d64.hip", "kvq_attend_d128.hip",
-           "kvq_geometry.hip", "kvq_fp8.hip"]
+           "kvq_geometry.hip", "kvq_fp8.hip", "kvq_scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -17,6 +17,7 @@ struct kvq {
     int32_t cus;            // compute units of the device the handle was made on
     int32_t force_splits;   // tuning overrides (KVQ_ATTEND_SPLITS / KVQ_ATTEND_WAVES), 0 = auto
     int32_t force_waves;
+    float* scratch;         // the library's static device scratch on the handle's device
 };
 
 namespace {
@@ -189,6 +190,98 @@ void attend_shape(const kvq* h, int n, int* splits_out, int* waves_out)
     *waves_out = waves;
 }
 
+// Decode attention over the geometry-ablation and FP8 caches: about
+// kTargetBlocks blocks, at least one 32-token chunk per split.
+bool other_path(const kvq* h)
+{
+    return h->cfg.geometry != 0 || h->cfg.format != KVQ_FORMAT_INT;
+}
+
+// Splits and waves of the decode attention at length n; `fused`: the launch
+// also appends token n-1 (threads 0 .. head_dim-1 of the last split).
+void plan_attend(const kvq* h, int n, bool fused, int* splits_out, int* waves_out)
+{
+    if (other_path(h)) {
+        const int rows = h->cfg.batch * h->cfg.q_heads;
+        const int chunks = (n + h->cfg.group - 1) / h->cfg.group;
+        int splits = (kTargetBlocks + rows - 1) / rows;
+        if (h->force_splits > 0) splits = h->force_splits;
+        if (splits > chunks) splits = chunks;
+        if (splits > h->layout.max_splits) splits = h->layout.max_splits;
+        if (splits < 1) splits = 1;
+        *splits_out = splits;
+        *waves_out = 0;
+        return;
+    }
+    attend_shape(h, n, splits_out, waves_out);
+    const int append_waves = h->cfg.head_dim / 64;
+    if (fused && *waves_out < append_waves)
+        *waves_out = append_waves;
+}
+
+// Bytes of split partials a launch with `splits` splits writes (none with
+// one split: it writes the output itself).
+size_t partial_bytes(const kvq* h, int splits)
+{
+    return splits > 1 ? (size_t)h->cfg.batch * h->cfg.q_heads * splits *
+                            (h->cfg.head_dim + 2) * sizeof(float)
+                      : 0;
+}
+
+// Enqueue the decode attention at length n (with k_new/v_new: the fused
+// append of token n-1).  The split partials go to the workspace's region,
+// or with use_static to the library's static scratch, packed with a stride
+// of `splits` per output row.
+int launch_attend(kvq* h, int n, int splits, int waves, const void* q, float* out,
+                  const void* k_new, const void* v_new, hipStream_t s, bool use_static)
+{
+    kvqi::Planes p = planes_of(h);
+    if (use_static) {
+        p.partials = h->scratch;
+        p.max_splits = splits;
+    }
+    if (other_path(h))
+        return hip_status(h->cfg.format == KVQ_FORMAT_FP8_E4M3
+                              ? kvqi::launch_attend_fp8(p, q, out, n, splits, s)
+                              : kvqi::launch_attend_geometry(p, q, out, n, splits, s));
+    return hip_status(h->cfg.head_dim == 64
+                          ? kvqi::launch_attend_d64(p, q, out, n, splits, waves, k_new, v_new, s)
+                          : kvqi::launch_attend_d128(p, q, out, n, splits, waves, k_new, v_new,
+                                                     s));
+}
+
+// One decode step: append, then attend.  One launch for a plain cache with
+// at most 4 query heads per KV head (one block per KV head), else the two
+// calls.  Everything is checked before anything is enqueued.
+int append_attend(kvq* h, const void* d_k, const void* d_v, const void* d_q, float* d_out,
+                  void* stream, bool use_static)
+{
+    if (!h || !d_k || !d_v || !d_q || !d_out)
+        return KVQ_ERR_ARG;
+    if (h->n >= h->cfg.max_tokens)
+        return KVQ_ERR_CAPACITY;
+    const int qpk_all = h->cfg.q_heads / h->cfg.kv_heads;
+    const bool fused = h->cfg.residual == 0 && h->cfg.sink == 0 && h->cfg.geometry == 0 &&
+                       h->cfg.format == KVQ_FORMAT_INT &&
+                       kvqi::block_heads(qpk_all) == qpk_all;  // one block per KV head
+    const int n = h->n + 1;
+    int splits, waves;
+    plan_attend(h, n, fused, &splits, &waves);
+    if (use_static && (!h->scratch || partial_bytes(h, splits) > kvqi::kStaticScratchBytes))
+        return h->scratch ? KVQ_ERR_SCRATCH : KVQ_ERR_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!fused) {
+        const int st = kvq_append_token(h, d_k, d_v, stream);
+        return st != KVQ_OK ? st
+                            : launch_attend(h, n, splits, waves, d_q, d_out, nullptr, nullptr, s,
+                                            use_static);
+    }
+    const int st = launch_attend(h, n, splits, waves, d_q, d_out, d_k, d_v, s, use_static);
+    if (st == KVQ_OK)
+        h->n = n;
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,6 +342,11 @@ int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes, kvq_t** out)
                   hipMemcpyHostToDevice) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess)
         return KVQ_ERR_HIP;
+    // the static scratch's address on this device, looked up once per device
+    int dev = 0;
+    void* scratch = nullptr;
+    if (hipGetDevice(&dev) != hipSuccess || kvqi::static_scratch(dev, &scratch) != hipSuccess)
+        return KVQ_ERR_HIP;
     kvq* h = new (std::nothrow) kvq;
     if (!h)
         return KVQ_ERR_ARG;
@@ -257,9 +355,9 @@ int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes, kvq_t** out)
     h->ws = ws;
     h->n = 0;
     h->cus = 0;
-    int dev = 0;
+    h->scratch = static_cast<float*>(scratch);
     hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
         h->cus = prop.multiProcessorCount;
     h->force_splits = env_int("KVQ_ATTEND_SPLITS");
     h->force_waves = env_int("KVQ_ATTEND_WAVES");
@@ -312,62 +410,22 @@ int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream)
         return KVQ_ERR_ARG;
     if (h->n == 0)
         return KVQ_ERR_STATE;
-    const int n = h->n;
-    const kvqi::Planes p = planes_of(h);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (h->cfg.geometry != 0 || h->cfg.format != KVQ_FORMAT_INT) {
-        // about kTargetBlocks blocks, at least one 32-token chunk per split
-        const int rows = h->cfg.batch * h->cfg.q_heads;
-        const int chunks = (n + h->cfg.group - 1) / h->cfg.group;
-        int splits = (kTargetBlocks + rows - 1) / rows;
-        if (h->force_splits > 0) splits = h->force_splits;
-        if (splits > chunks) splits = chunks;
-        if (splits > h->layout.max_splits) splits = h->layout.max_splits;
-        if (splits < 1) splits = 1;
-        return hip_status(h->cfg.format == KVQ_FORMAT_FP8_E4M3
-                              ? kvqi::launch_attend_fp8(p, d_q, d_out, n, splits, s)
-                              : kvqi::launch_attend_geometry(p, d_q, d_out, n, splits, s));
-    }
     int splits, waves;
-    attend_shape(h, n, &splits, &waves);
-    return hip_status(h->cfg.head_dim == 64
-                          ? kvqi::launch_attend_d64(p, d_q, d_out, n, splits, waves,
-                                                    nullptr, nullptr, s)
-                          : kvqi::launch_attend_d128(p, d_q, d_out, n, splits, waves,
-                                                     nullptr, nullptr, s));
+    plan_attend(h, h->n, false, &splits, &waves);
+    return launch_attend(h, h->n, splits, waves, d_q, d_out, nullptr, nullptr,
+                         static_cast<hipStream_t>(stream), false);
 }
 
 int kvq_append_attend(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
                       float* d_out, void* stream)
 {
-    if (!h || !d_k || !d_v || !d_q || !d_out)
-        return KVQ_ERR_ARG;
-    if (h->n >= h->cfg.max_tokens)
-        return KVQ_ERR_CAPACITY;
-    const int qpk_all = h->cfg.q_heads / h->cfg.kv_heads;
-    const bool fused = h->cfg.residual == 0 && h->cfg.sink == 0 && h->cfg.geometry == 0 &&
-                       h->cfg.format == KVQ_FORMAT_INT &&
-                       kvqi::block_heads(qpk_all) == qpk_all;  // one block per KV head
-    if (!fused) {
-        const int st = kvq_append_token(h, d_k, d_v, stream);
-        return st != KVQ_OK ? st : kvq_attend_decode(h, d_q, d_out, stream);
-    }
-    const int n = h->n + 1;
-    const kvqi::Planes p = planes_of(h);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int splits, waves;
-    attend_shape(h, n, &splits, &waves);
-    const int append_waves = h->cfg.head_dim / 64;  // threads 0..head_dim-1 append
-    if (waves < append_waves)
-        waves = append_waves;
-    const int st = hip_status(h->cfg.head_dim == 64
-                                  ? kvqi::launch_attend_d64(p, d_q, d_out, n, splits, waves,
-                                                            d_k, d_v, s)
-                                  : kvqi::launch_attend_d128(p, d_q, d_out, n, splits, waves,
-                                                             d_k, d_v, s));
-    if (st == KVQ_OK)
-        h->n = n;
-    return st;
+    return append_attend(h, d_k, d_v, d_q, d_out, stream, false);
+}
+
+int kvq_append_attend_static(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
+                             float* d_out, void* stream)
+{
+    return append_attend(h, d_k, d_v, d_q, d_out, stream, true);
 }
 
 int kvq_error_metrics(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
@@ -411,6 +469,7 @@ const char* kvq_strerror(int status)
     case KVQ_ERR_STATE: return "call not valid in the cache's current state";
     case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
     case KVQ_ERR_HIP: return "HIP runtime error";
+    case KVQ_ERR_SCRATCH: return "the call needs more than the library's static device scratch";
     default: return "unknown status";
     }
 }

@@ -2,6 +2,8 @@
 // the gfx950 kernels (kvq_kernels.hip).  Not part of the public ABI.
 #pragma once
 
+#include "kvq.h"
+
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -68,6 +70,14 @@ __host__ __device__ inline int quantized_end(int n, int residual, int sink)
     const int q = quantized_tokens(n, residual);
     return q > s ? q : s;
 }
+
+// Bytes of the library's static device scratch (kvq_scratch.hip), which
+// holds the split partials of kvq_append_attend_static.
+constexpr size_t kStaticScratchBytes = KVQ_STATIC_SCRATCH_BYTES;
+
+// Device address of that scratch on `device`, which must be current; looked
+// up once per device and kept.
+hipError_t static_scratch(int device, void** out);
 
 // Launch wrappers (kvq_kernels.hip).  All enqueue on `stream` and return the
 // hipGetLastError() status of the launches.
