@@ -1,8 +1,10 @@
 """kvq_append_attend_static (split partials in the library's static device
 scratch, no allocation) against kvq_append_attend (partials in the
 workspace) through the C ABI: identically prefilled caches, the same decode
-steps, outputs and planes compared bit for bit (same kernels, same launch
-shape), and the output against the oracle within the attention tolerance.
+steps, planes compared bit for bit, outputs bit for bit where the kernels sum
+in a fixed order (one query head per KV head) and to fp32 rounding where
+they do not, and the output against the oracle within the attention
+tolerance.
 Calls in a row on one GPU share the scratch: a large step (many splits)
 followed by smaller ones."""
 import os
@@ -57,10 +59,19 @@ def _run(cfg, n0, cap, fmt=None, **kw):
     if fmt is not None:
         extra["format"] = fmt
     caches, k, v = _pair(cfg, n0, cap, **extra)
+    # One query head per KV head: both paths sum in the same fixed order, so
+    # their outputs agree bit for bit.  With several, waves take groups as
+    # they become ready and the order varies between calls: the outputs then
+    # agree to fp32 rounding, far inside the attention tolerance.
+    exact = cfg.q_heads == cfg.kv_heads or fmt is not None
     for s in range(2):
         a, b = _step_both(cfg, caches, k, v, n0 + s, s)
         assert np.isfinite(a).all()
-        assert np.array_equal(a, b), "static-scratch output differs from the workspace path"
+        if exact:
+            assert np.array_equal(a, b), "static-scratch output differs from the workspace path"
+        else:
+            assert np.abs(a - b).max() <= 1e-5 * np.abs(a).max(), \
+                "static-scratch output differs from the workspace path"
     n = n0 + 2
     assert len(caches[0]) == len(caches[1]) == n
     ga, gb = gpu_planes(caches[0]), gpu_planes(caches[1])
