@@ -41,6 +41,14 @@ __device__ __forceinline__ void append_token_groups(uint32_t* __restrict__ codes
         mn = fminf(mn, __shfl_xor(mn, off));
         mx = fmaxf(mx, __shfl_xor(mx, off));
     }
+    // the zero point is the first minimal element: for a zero minimum the
+    // first zero in channel order gives its sign (the condition holds for all
+    // 32 lanes of the group or none)
+    if (mn == 0.0f) {
+        const unsigned long long zb = __ballot(x == 0.0f);
+        const int base = (threadIdx.x & 63) & ~31;
+        mn = __shfl(x, base + __builtin_ctz((uint32_t)(zb >> base)));
+    }
     const GroupParams gp = group_params(mn, mx, BITS);
     const int j = c % kGroup;
     uint32_t bits = code_of_fast(x, gp, (1 << BITS) - 1) << ((j * BITS) % 32);

@@ -17,6 +17,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 namespace kvqi {
 namespace {
 
@@ -31,9 +33,21 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h)
 
 // ------------------------------------------------------- prefill kernels --
 
-// One thread per (sequence*head, key group, channel): walks the group's G
-// tokens down the channel, so the per-channel statistics need no cross-lane
-// reduction; consecutive threads read consecutive channels of a token row.
+// Key groups per 256-thread block: a thread takes one channel of a group
+// (fp32 inputs) or two adjacent channels (binary16 inputs: one 32-bit load
+// per token, both channels' statistics on packed pairs).
+template <typename T>
+__host__ __device__ constexpr int key_groups_per_block(int D)
+{
+    return std::is_same<T, __half>::value ? 512 / D : 256 / D;
+}
+
+// One thread per (sequence*head, key group, channel or channel pair): walks
+// the group's G tokens down the channel, so the per-channel statistics need
+// no cross-lane reduction; consecutive threads read consecutive channels of
+// a token row.  Block bx of sequence/head bh covers key groups
+// g_begin + bx * key_groups_per_block .. ; per-sequence bases are uniform,
+// per-thread offsets 32-bit (a sequence/head holds under 2^31 elements).
 template <typename T, int BITS>
 __device__ __forceinline__ void quant_keys_block(const Planes& p, const T* __restrict__ k,
                                                  int n_tokens, int g_begin, int g_end, int bx,
@@ -41,24 +55,50 @@ __device__ __forceinline__ void quant_keys_block(const Planes& p, const T* __res
 {
     constexpr int WK = G * BITS / 32;
     const int D = p.D;
+    const T* kb = k + bh * (size_t)n_tokens * D;
+    uint32_t* cb = p.k_codes + bh * (size_t)p.gcap * D * WK;
+    uint32_t* mb = p.k_meta + bh * (size_t)p.gcap * D;
+    if constexpr (std::is_same<T, __half>::value) {
+        const int np = D / 2;  // channel pairs
+        const int cp = threadIdx.x % np;
+        const int g = g_begin + bx * key_groups_per_block<T>(D) + threadIdx.x / np;
+        if (g >= g_end)
+            return;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(kb) + (uint32_t)(g * G * np + cp);
+        uint32_t d[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            d[j] = src[j * np];
+        uint32_t w0[WK], w1[WK], m0, m1;
+        quantize_group_two<BITS>(d, w0, w1, m0, m1);
+        const uint32_t gc = (uint32_t)(g * D + 2 * cp);  // channel 2cp; 2cp+1 follows
+        uint32_t* dst = cb + gc * WK;
+#pragma unroll
+        for (int i = 0; i < WK; ++i) {
+            dst[i] = w0[i];
+            dst[WK + i] = w1[i];
+        }
+        *reinterpret_cast<uint2*>(mb + gc) = make_uint2(m0, m1);
+        return;
+    }
     const int gpb = blockDim.x / D;
     const int c = threadIdx.x % D;
     const int g = g_begin + bx * gpb + threadIdx.x / D;
     if (g >= g_end)
         return;
-    const T* src = k + (bh * (size_t)n_tokens + (size_t)g * G) * D + c;
+    const T* src = kb + (uint32_t)(g * G * D + c);
     float x[G];
 #pragma unroll
     for (int j = 0; j < G; ++j)
-        x[j] = to_f32(src[(size_t)j * D]);
+        x[j] = to_f32(src[j * D]);
     uint32_t w[WK];
     const uint32_t meta = quantize_group<BITS>(x, w);
-    const size_t gc = (bh * p.gcap + g) * D + c;
-    uint32_t* dst = p.k_codes + gc * WK;
+    const uint32_t gc = (uint32_t)(g * D + c);
+    uint32_t* dst = cb + gc * WK;
 #pragma unroll
     for (int i = 0; i < WK; ++i)
         dst[i] = w[i];
-    p.k_meta[gc] = meta;
+    mb[gc] = meta;
 }
 
 template <typename T, int BITS>
@@ -86,59 +126,85 @@ __global__ void copy_tail_kernel(Planes p, const T* __restrict__ src, T* __restr
     dst[(bh * slots + t % slots) * D + c] = src[(bh * n_tokens + t) * D + c];
 }
 
+// Value groups per 256-thread block row: block bx of sequence/head bh takes
+// the groups (token t, channel group cg) with t * (D/G) + cg in
+// [256 bx, 256 bx + 256).
+__host__ __device__ constexpr int value_blocks(int n_src, int D)
+{
+    return (n_src * (D / G) + 255) / 256;
+}
+
 // One thread per (sequence*head, token, channel group): the group is G
 // consecutive channels of one token row (64 contiguous bytes at fp16).
 // Input tokens [0, n_src) of rows of src_stride tokens go to cache slots
-// [t_dst0, t_dst0 + n_src).
+// [t_dst0, t_dst0 + n_src); the thread's group is number
+// 256 bx + threadIdx.x of sequence/head bh.
 template <typename T, int BITS>
 __device__ __forceinline__ void quant_values_thread(const Planes& p, const T* __restrict__ v,
-                                                    int n_src, int src_stride, int t_dst0,
-                                                    size_t total, size_t idx)
+                                                    int n_src, int src_stride, int t_dst0, int bx,
+                                                    size_t bh)
 {
     constexpr int WV = G * BITS / 32;
-    if (idx >= total)
-        return;
     const int D = p.D;
-    const int ncg = D / G;
-    const int cg = idx % ncg;
-    const size_t r = idx / ncg;
-    const int t = r % n_src;
-    const size_t bh = r / n_src;
-    const T* src = v + (bh * src_stride + t) * D + (size_t)cg * G;
-    float x[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-        x[j] = to_f32(src[j]);
+    const int cg_bits = D == 128 ? 2 : 1;  // D / G = 4 or 2 channel groups
+    const uint32_t local = (uint32_t)bx * 256u + threadIdx.x;
+    if (local >= (uint32_t)n_src << cg_bits)
+        return;
+    const uint32_t t = local >> cg_bits, cg = local & ((1u << cg_bits) - 1u);
+    const T* src = v + bh * (size_t)src_stride * D + (t * (uint32_t)D + cg * G);
+    const size_t row0 = bh * (size_t)p.tcap + t_dst0;  // first destination token row
+    uint32_t* dst = p.v_codes + (row0 << cg_bits) * WV + local * WV;
+    uint32_t* mdst = p.v_meta + (row0 << cg_bits) + local;
     uint32_t w[WV];
-    const uint32_t meta = quantize_group<BITS>(x, w);
-    const size_t tc = (bh * p.tcap + t_dst0 + t) * ncg + cg;
-    uint32_t* dst = p.v_codes + tc * WV;
+    uint32_t meta;
+    if constexpr (std::is_same<T, __half>::value) {
+        // 64 contiguous bytes (16-byte aligned: rows of D >= 64 binary16)
+        uint32_t d[G / 2];
+#pragma unroll
+        for (int i = 0; i < G / 8; ++i) {
+            const uint4 q = reinterpret_cast<const uint4*>(src)[i];
+            d[4 * i] = q.x;
+            d[4 * i + 1] = q.y;
+            d[4 * i + 2] = q.z;
+            d[4 * i + 3] = q.w;
+        }
+        meta = quantize_group_pairs<BITS>(d, w);
+    } else {
+        float x[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            x[j] = to_f32(src[j]);
+        meta = quantize_group<BITS>(x, w);
+    }
 #pragma unroll
     for (int i = 0; i < WV; ++i)
         dst[i] = w[i];
-    p.v_meta[tc] = meta;
+    *mdst = meta;
 }
 
+// grid (value_blocks(n_src, D), sequences/heads in this launch); bh0 = the
+// first sequence/head
 template <typename T, int BITS>
 __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __restrict__ v,
                                                            int n_src, int src_stride, int t_dst0,
-                                                           size_t total)
+                                                           size_t bh0)
 {
-    quant_values_thread<T, BITS>(p, v, n_src, src_stride, t_dst0, total,
-                                 (size_t)blockIdx.x * blockDim.x + threadIdx.x);
+    quant_values_thread<T, BITS>(p, v, n_src, src_stride, t_dst0, blockIdx.x,
+                                 bh0 + blockIdx.y);
 }
 
 // Keys and values of a prefill in one launch: the two codecs read disjoint
 // inputs and write disjoint planes, so their blocks interleave (even blocks
 // keys, odd blocks values while both last) and the two streams overlap
 // instead of running one after the other.  Key block kb covers key-group
-// block kb % kgx of sequence/head kb / kgx.
+// block kb % kgx of sequence/head kb / kgx, value block vb value block
+// vb % vbx of sequence/head vb / vbx.
 template <typename T, int KB, int VB>
 __global__ __launch_bounds__(256) void quant_kv_kernel(Planes p, const T* __restrict__ k,
                                                        int n_tokens, int g_begin, int g_end,
                                                        int kgx, unsigned kblocks,
                                                        const T* __restrict__ v, int n_src,
-                                                       int t_dst0, size_t vtotal, unsigned vblocks)
+                                                       int t_dst0, int vbx, unsigned vblocks)
 {
     const unsigned b = blockIdx.x;
     const unsigned both = 2u * (kblocks < vblocks ? kblocks : vblocks);
@@ -155,8 +221,8 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(Planes p, const T* __rest
         quant_keys_block<T, KB>(p, k, n_tokens, g_begin, g_end, (int)(i % (unsigned)kgx),
                                 i / (unsigned)kgx);
     else
-        quant_values_thread<T, VB>(p, v, n_src, n_tokens, t_dst0, vtotal,
-                                   (size_t)i * blockDim.x + threadIdx.x);
+        quant_values_thread<T, VB>(p, v, n_src, n_tokens, t_dst0, (int)(i % (unsigned)vbx),
+                                   i / (unsigned)vbx);
 }
 
 // Append one token per sequence/head in one launch (block = one sequence/head,
@@ -284,12 +350,32 @@ void quantize_channel_groups(Planes q, uint32_t* codes, uint32_t* meta, int bits
         return;
     q.k_codes = codes;
     q.k_meta = meta;
-    const int gpb = 256 / q.D;
+    const int gpb = key_groups_per_block<T>(q.D);
     dim3 grid((g_end - g_begin + gpb - 1) / gpb, q.nb * q.hkv);
     switch (bits) {
-    case 2: quant_keys_kernel<T, 2><<<grid, gpb * q.D, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
-    case 4: quant_keys_kernel<T, 4><<<grid, gpb * q.D, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
-    case 8: quant_keys_kernel<T, 8><<<grid, gpb * q.D, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    case 2: quant_keys_kernel<T, 2><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    case 4: quant_keys_kernel<T, 4><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    case 8: quant_keys_kernel<T, 8><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    }
+}
+
+// The value codec over tokens [0, n_src) (rows of src_stride tokens from
+// src) of every sequence/head into slots [t_dst0, t_dst0 + n_src) of the
+// planes in q.v_codes / q.v_meta (at most 65535 sequences/heads per launch).
+template <typename T>
+void launch_token_groups(const Planes& q, int bits, const T* src, int n_src, int src_stride,
+                         int t_dst0, hipStream_t stream)
+{
+    if (n_src <= 0)
+        return;
+    const int nbh = q.nb * q.hkv;
+    for (int bh0 = 0; bh0 < nbh; bh0 += 65535) {
+        const dim3 grid(value_blocks(n_src, q.D), nbh - bh0 < 65535 ? nbh - bh0 : 65535);
+        switch (bits) {
+        case 2: quant_values_kernel<T, 2><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
+        case 4: quant_values_kernel<T, 4><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
+        case 8: quant_values_kernel<T, 8><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
+        }
     }
 }
 
@@ -297,17 +383,9 @@ template <typename T>
 void quantize_token_groups(Planes q, uint32_t* codes, uint32_t* meta, int bits, const T* src,
                            int n_src, int src_stride, int t_dst0, hipStream_t stream)
 {
-    const size_t total = n_src > 0 ? (size_t)q.nb * q.hkv * n_src * (q.D / G) : 0;
-    if (total == 0)
-        return;
     q.v_codes = codes;
     q.v_meta = meta;
-    const unsigned blocks = (unsigned)((total + 255) / 256);
-    switch (bits) {
-    case 2: quant_values_kernel<T, 2><<<blocks, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, total); break;
-    case 4: quant_values_kernel<T, 4><<<blocks, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, total); break;
-    case 8: quant_values_kernel<T, 8><<<blocks, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, total); break;
-    }
+    launch_token_groups<T>(q, bits, src, n_src, src_stride, t_dst0, stream);
 }
 
 template <typename T>
@@ -358,20 +436,20 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
     // [S, tq) quantized and the rest copied to the value ring
     const int vq = p.residual > 0 ? tq : n_tokens;
     const int v0 = ns;  // first quantized value token (S, or n_tokens while n_tokens < S)
-    const size_t vg = vq > v0 ? (size_t)nbh * (vq - v0) * (p.D / G) : 0;
-    const unsigned vblocks = (unsigned)((vg + 255) / 256);
+    const int vbx = vq > v0 ? value_blocks(vq - v0, p.D) : 0;
+    const size_t vblocks = (size_t)vbx * nbh;
     const T* vsrc = v + (size_t)v0 * p.D;  // token v0 of sequence/head 0; rows of n_tokens
-    const int gpb = 256 / p.D;
+    const int gpb = key_groups_per_block<T>(p.D);
     const int kgx = g_end > g_begin ? (g_end - g_begin + gpb - 1) / gpb : 0;
-    const unsigned kblocks = (unsigned)kgx * (unsigned)nbh;
+    const size_t kblocks = (size_t)kgx * nbh;
     bool values_done = false;
-    if (kblocks > 0 && vblocks > 0 && gpb * p.D == 256) {
+    if (kblocks > 0 && vblocks > 0 && kblocks + vblocks <= (size_t)UINT32_MAX) {
         // both codecs in one launch
-        const unsigned blocks = kblocks + vblocks;
+        const unsigned blocks = (unsigned)(kblocks + vblocks);
 #define KVQ_KV(KBB, VBB)                                                                     \
     quant_kv_kernel<T, KBB, VBB><<<blocks, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end, \
-                                                             kgx, kblocks, vsrc, vq - v0, v0,   \
-                                                             vg, vblocks)
+                                                             kgx, (unsigned)kblocks, vsrc,     \
+                                                             vq - v0, v0, vbx, (unsigned)vblocks)
         switch (p.kbits * 16 + p.vbits) {
         case 2 * 16 + 2: KVQ_KV(2, 2); break;
         case 2 * 16 + 4: KVQ_KV(2, 4); break;
@@ -388,9 +466,9 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
     } else if (kblocks > 0) {
         dim3 grid(kgx, nbh);
         switch (p.kbits) {
-        case 2: quant_keys_kernel<T, 2><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
-        case 4: quant_keys_kernel<T, 4><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
-        case 8: quant_keys_kernel<T, 8><<<grid, gpb * p.D, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
+        case 2: quant_keys_kernel<T, 2><<<grid, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
+        case 4: quant_keys_kernel<T, 4><<<grid, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
+        case 8: quant_keys_kernel<T, 8><<<grid, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
         }
     }
     auto copy = [&](const T* src, void* dst, int slots, int t0, int t1) {
@@ -404,13 +482,8 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
     copy(v, p.v_sink, p.sink, 0, ns);
     if (p.residual > 0)
         copy(v, p.v_tail, p.ring, tq, n_tokens);
-    if (vg > 0 && !values_done) {
-        switch (p.vbits) {
-        case 2: quant_values_kernel<T, 2><<<vblocks, 256, 0, stream>>>(p, vsrc, vq - v0, n_tokens, v0, vg); break;
-        case 4: quant_values_kernel<T, 4><<<vblocks, 256, 0, stream>>>(p, vsrc, vq - v0, n_tokens, v0, vg); break;
-        case 8: quant_values_kernel<T, 8><<<vblocks, 256, 0, stream>>>(p, vsrc, vq - v0, n_tokens, v0, vg); break;
-        }
-    }
+    if (vblocks > 0 && !values_done)
+        launch_token_groups<T>(p, p.vbits, vsrc, vq - v0, n_tokens, v0, stream);
     return hipGetLastError();
 }
 

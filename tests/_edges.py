@@ -21,10 +21,12 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "qua
 
 
 def _exact(vals, dtype):
-    """vals (float64) as `dtype`, asserting that each value is exact."""
+    """vals (float64) as `dtype`, asserting that each value is exact (signs of
+    zero included)."""
     a = np.asarray(vals, dtype=np.float64)
     b = a.astype(dtype)
-    assert np.array_equal(b.astype(np.float64), a), f"not exact in {np.dtype(dtype)}: {a}"
+    assert np.array_equal(b.astype(np.float64), a) and \
+        np.array_equal(np.signbit(b), np.signbit(a)), f"not exact in {np.dtype(dtype)}: {a}"
     return b
 
 
@@ -119,6 +121,13 @@ def edge_groups(bits: int, dtype=np.float16, seed: int = 0):
     # for top >= 3), codes all 0 although the group is not constant
     add("zero_step_a", _fill([0.0, sub], [0.0, sub]))
     add("zero_step_b", _fill([2.0 ** -14, 2.0 ** -14 + sub], [2.0 ** -14, 2.0 ** -14 + sub]))
+
+    # zero minima with both signs of zero: the zero point is the first
+    # minimal element, so its sign is that of the first zero in index order
+    # (the tilers rotate groups, so both orders occur)
+    add("zeros_neg_first", _fill([-0.0, 0.0, 1.0, 2.0], [0.5, 1.5, 0.0, -0.0, 3.0]))
+    add("zeros_pos_first", _fill([0.0, -0.0, 3.0], [-0.0, 1.0, 0.0, 2.5]))
+    add("all_zeros_mixed", _fill([-0.0, 0.0], [0.0, -0.0]))
 
     # large magnitudes, both signs
     big = np.round(rng.uniform(-60000, 60000, G - 2))

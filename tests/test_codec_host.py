@@ -29,6 +29,13 @@ def shim(tmp_path_factory):
         f.restype = ctypes.c_uint32
     L.shim_fallbacks.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
     L.shim_fallbacks.restype = ctypes.c_int
+    L.shim_quant_pairs.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.shim_quant_pairs.restype = ctypes.c_uint32
+    L.shim_quant_two.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    L.shim_quant_two.restype = None
+    L.shim_half_step.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_int]
+    L.shim_half_step.restype = ctypes.c_uint32
     return L
 
 
@@ -113,3 +120,110 @@ def _nudge(v, steps, dt):
     for _ in range(abs(int(steps))):
         v = np.nextafter(v, d, dtype=dt)
     return v
+
+
+def _f16_groups(rng, bits):
+    """Random binary16 groups over many scales (some with an outlier), exact
+    ties, near ties and the edge-case groups of tests/_edges.py."""
+    from _edges import edge_groups
+    groups = []
+    for _ in range(2000):
+        x = rng.standard_normal(32) * 10.0 ** rng.uniform(-4, 3)
+        if rng.random() < 0.3:
+            x[rng.integers(32)] *= 50
+        with np.errstate(over="ignore"):
+            x = x.astype(np.float16)
+        if np.all(np.isfinite(x)) and (float(x.max()) - float(x.min())) / (2 ** bits - 1) < 65504:
+            groups.append(x)
+    for _ in range(300):
+        s = 2.0 ** rng.integers(-8, 3)
+        z = float(np.float16(rng.integers(-64, 64) * s))
+        top = 2 ** bits - 1
+        x = np.concatenate([[z, z + top * s], z + (rng.integers(0, top, 30) + 0.5) * s])
+        groups.append(x.astype(np.float16))
+    groups += _near_ties(rng, bits, np.float16)
+    _, eg = edge_groups(bits, np.float16)
+    for g in eg:  # every rotation of each edge group, as the GPU tilers use them
+        for r in range(0, 32, 5):
+            groups.append(np.roll(g, r))
+    return groups
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_binary16_step_rounding(shim, bits):
+    """The binary16 codec's step (an fp64 product with the rounded 1/(2^B-1),
+    then round-to-odd through fp32) is the binary16 nearest to the exact
+    range/(2^B-1), ties to even: checked against exact rational rounding at
+    every binary16 rounding boundary times 2^B-1 (the exact ties), a few
+    2^-24 either side of them, over every binade, and at random ranges."""
+    from fractions import Fraction
+    from test_oracle_edges import _rne16
+    top = 2 ** bits - 1
+    rng = np.random.default_rng(7 + bits)
+    ds = []
+    for e in range(-24, 16):  # binade [2^e, 2^(e+1)) of the quotient
+        spacing = Fraction(2) ** max(e - 10, -24)
+        for j in list(range(4)) + list(rng.integers(0, 1 << 10, 12)):
+            m = Fraction(2) ** e + (Fraction(2 * int(j) + 1, 2)) * spacing  # a boundary
+            for k in (-3, -1, 0, 1, 2):
+                d = top * m + k * Fraction(1, 1 << 24)
+                if 0 <= d < 2 ** 17:
+                    ds.append(d)
+    for _ in range(3000):
+        ds.append(Fraction(int(rng.integers(0, 1 << 41)), 1 << 24))
+    for d in ds:
+        # mx - mn = d from two fp32 values (integer part, fraction of 2^-24)
+        ip = Fraction(int(d))
+        mx, mn = np.float32(float(ip)), np.float32(-float(d - ip))
+        assert Fraction(float(mx)) - Fraction(float(mn)) == d
+        got = shim.shim_half_step(float(mn), float(mx), bits)
+        want = _rne16(d / top)
+        assert got == want, (bits, float(d), hex(got), hex(want))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_binary16_codec_matches_oracle(shim, orc, bits):
+    """The binary16-input group codec of the prefill kernels (packed-pair
+    minimum and maximum, zero point from the first minimal element, codes
+    without a clamp for a normal step) equals the oracle, for one group in 16
+    packed words and for two groups in the two halves of 32 words."""
+    rng = np.random.default_rng(100 + bits)
+    groups = _f16_groups(rng, bits)
+    want = [orc.quant_group(x.astype(np.float64), bits) for x in groups]
+    for x, (oc, s16, z16) in zip(groups, want):
+        codes = np.zeros(32, dtype=np.uint8)
+        meta = shim.shim_quant_pairs(np.ascontiguousarray(x).view(np.uint32).ctypes.data, bits,
+                                     codes.ctypes.data)
+        assert meta == (s16 | (z16 << 16)), (x, hex(meta), hex(s16 | (z16 << 16)))
+        assert np.array_equal(codes, oc)
+    for a in range(0, len(groups) - 1, 2):
+        x0, x1 = groups[a], groups[a + 1]
+        words = (x0.view(np.uint16).astype(np.uint32) |
+                 (x1.view(np.uint16).astype(np.uint32) << 16))
+        c0 = np.zeros(32, dtype=np.uint8)
+        c1 = np.zeros(32, dtype=np.uint8)
+        metas = np.zeros(2, dtype=np.uint32)
+        shim.shim_quant_two(np.ascontiguousarray(words).ctypes.data, bits, c0.ctypes.data,
+                            c1.ctypes.data, metas.ctypes.data)
+        for (oc, s16, z16), c, m in ((want[a], c0, metas[0]), (want[a + 1], c1, metas[1])):
+            assert m == (s16 | (z16 << 16))
+            assert np.array_equal(c, oc)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_float_codec_on_edge_groups(shim, orc, bits, dt):
+    """The fp32-input group quantizer (fp32 caches, appends, window flushes)
+    on the edge-case groups in every rotation, zero minima of both signs
+    included."""
+    from _edges import edge_groups
+    _, eg = edge_groups(bits, dt)
+    for g in eg:
+        for r in range(0, 32, 3):
+            x = np.roll(g, r)
+            xf = np.ascontiguousarray(x.astype(np.float32))
+            oc, s16, z16 = orc.quant_group(x.astype(np.float64), bits)
+            codes = np.zeros(32, dtype=np.uint8)
+            meta = shim.shim_quant_group(xf.ctypes.data, 32, bits, codes.ctypes.data)
+            assert meta == (s16 | (z16 << 16)), (x, hex(meta), hex(s16 | (z16 << 16)))
+            assert np.array_equal(codes, oc)

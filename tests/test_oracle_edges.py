@@ -35,7 +35,10 @@ def _rne16(fr):
 def _brute(x, bits):
     fx = [Fraction(float(v)) for v in x]
     mn, mx = min(fx), max(fx)
-    z16 = _rne16(mn)
+    # the zero point is the first minimal element: for a zero minimum that
+    # element's sign of zero (a Fraction has none)
+    first = next(v for v, f in zip(x, fx) if f == mn)
+    z16 = _rne16(mn) | (0x8000 if mn == 0 and np.signbit(first) else 0)
     s16 = _rne16((mx - mn) / (2 ** bits - 1))
     z, s = _half(z16), _half(s16)
     codes = []
@@ -54,9 +57,7 @@ def test_edge_groups_against_exact_arithmetic(orc, bits, dtype):
     for name, x in zip(names, groups):
         codes, s16, z16 = orc.quant_group(x.astype(np.float64), bits)
         want_codes, want_s, want_z = _brute(x, bits)
-        # -0 and +0 are the same zero point; the oracle stores +0 for a zero minimum
-        assert (z16 & 0x7FFF or 0) == (want_z & 0x7FFF or 0) and \
-            (z16 == want_z or _half(z16) == 0), f"{name}: zero {z16:#06x} != {want_z:#06x}"
+        assert z16 == want_z, f"{name}: zero {z16:#06x} != {want_z:#06x}"
         assert s16 == want_s, f"{name}: step {s16:#06x} != {want_s:#06x}"
         assert codes.tolist() == want_codes, f"{name}: codes differ"
 
@@ -87,5 +88,7 @@ def test_edge_groups_reach_the_corners(orc):
                     seen.add("zero_range")
                 if np.dtype(dtype) == np.float32 and z != min(fx):
                     seen.add("f32_zero_not_min")
+                if z16 == 0x8000:
+                    seen.add("negative_zero_point")
     assert seen >= {"tie", "zero_step_nonconstant", "subnormal_step", "step_rounding_tie",
-                    "zero_range", "f32_zero_not_min"}, seen
+                    "zero_range", "f32_zero_not_min", "negative_zero_point"}, seen
