@@ -48,18 +48,17 @@ __host__ __device__ constexpr int key_groups_per_block(int D)
 // a token row.  Block bx of sequence/head bh covers key groups
 // g_begin + bx * key_groups_per_block .. ; per-sequence bases are uniform,
 // per-thread offsets 32-bit (a sequence/head holds under 2^31 elements).
-template <typename T, int BITS>
+template <typename T, int BITS, int D>
 __device__ __forceinline__ void quant_keys_block(const Planes& p, const T* __restrict__ k,
                                                  int n_tokens, int g_begin, int g_end, int bx,
                                                  size_t bh)
 {
     constexpr int WK = G * BITS / 32;
-    const int D = p.D;
     const T* kb = k + bh * (size_t)n_tokens * D;
     uint32_t* cb = p.k_codes + bh * (size_t)p.gcap * D * WK;
     uint32_t* mb = p.k_meta + bh * (size_t)p.gcap * D;
     if constexpr (std::is_same<T, __half>::value) {
-        const int np = D / 2;  // channel pairs
+        constexpr int np = D / 2;  // channel pairs
         const int cp = threadIdx.x % np;
         const int g = g_begin + bx * key_groups_per_block<T>(D) + threadIdx.x / np;
         if (g >= g_end)
@@ -81,7 +80,7 @@ __device__ __forceinline__ void quant_keys_block(const Planes& p, const T* __res
         *reinterpret_cast<uint2*>(mb + gc) = make_uint2(m0, m1);
         return;
     }
-    const int gpb = blockDim.x / D;
+    constexpr int gpb = 256 / D;
     const int c = threadIdx.x % D;
     const int g = g_begin + bx * gpb + threadIdx.x / D;
     if (g >= g_end)
@@ -101,11 +100,11 @@ __device__ __forceinline__ void quant_keys_block(const Planes& p, const T* __res
     mb[gc] = meta;
 }
 
-template <typename T, int BITS>
+template <typename T, int BITS, int D>
 __global__ __launch_bounds__(256) void quant_keys_kernel(Planes p, const T* __restrict__ k,
                                                          int n_tokens, int g_begin, int g_end)
 {
-    quant_keys_block<T, BITS>(p, k, n_tokens, g_begin, g_end, blockIdx.x, blockIdx.y);
+    quant_keys_block<T, BITS, D>(p, k, n_tokens, g_begin, g_end, blockIdx.x, blockIdx.y);
 }
 
 // Copy tokens [t0, t1) of each sequence/head verbatim into a buffer of
@@ -139,14 +138,13 @@ __host__ __device__ constexpr int value_blocks(int n_src, int D)
 // Input tokens [0, n_src) of rows of src_stride tokens go to cache slots
 // [t_dst0, t_dst0 + n_src); the thread's group is number
 // 256 bx + threadIdx.x of sequence/head bh.
-template <typename T, int BITS>
+template <typename T, int BITS, int D>
 __device__ __forceinline__ void quant_values_thread(const Planes& p, const T* __restrict__ v,
                                                     int n_src, int src_stride, int t_dst0, int bx,
                                                     size_t bh)
 {
     constexpr int WV = G * BITS / 32;
-    const int D = p.D;
-    const int cg_bits = D == 128 ? 2 : 1;  // D / G = 4 or 2 channel groups
+    constexpr int cg_bits = D == 128 ? 2 : 1;  // D / G = 4 or 2 channel groups
     const uint32_t local = (uint32_t)bx * 256u + threadIdx.x;
     if (local >= (uint32_t)n_src << cg_bits)
         return;
@@ -184,45 +182,39 @@ __device__ __forceinline__ void quant_values_thread(const Planes& p, const T* __
 
 // grid (value_blocks(n_src, D), sequences/heads in this launch); bh0 = the
 // first sequence/head
-template <typename T, int BITS>
+template <typename T, int BITS, int D>
 __global__ __launch_bounds__(256) void quant_values_kernel(Planes p, const T* __restrict__ v,
                                                            int n_src, int src_stride, int t_dst0,
                                                            size_t bh0)
 {
-    quant_values_thread<T, BITS>(p, v, n_src, src_stride, t_dst0, blockIdx.x,
-                                 bh0 + blockIdx.y);
+    quant_values_thread<T, BITS, D>(p, v, n_src, src_stride, t_dst0, blockIdx.x,
+                                    bh0 + blockIdx.y);
 }
 
-// Keys and values of a prefill in one launch: the two codecs read disjoint
-// inputs and write disjoint planes, so their blocks interleave (even blocks
-// keys, odd blocks values while both last) and the two streams overlap
-// instead of running one after the other.  Key block kb covers key-group
-// block kb % kgx of sequence/head kb / kgx, value block vb value block
-// vb % vbx of sequence/head vb / vbx.
-template <typename T, int KB, int VB>
+// Keys and values of a prefill in one launch: blocks [0, kblocks) run the
+// key codec (block kb: key-group block kb % kgx of sequence/head kb / kgx),
+// the rest the value codec (value block vb % vbx of sequence/head vb / vbx,
+// vb = block - kblocks).  Keys first, then values: on the Llama-2-7B-shaped
+// prompt (8 x 32 heads x 4095 tokens x 128, fp16) this measured 121 us
+// against 133 us with key and value blocks alternating and 128 us as two
+// launches; the one launch lets the last key blocks overlap the first value
+// blocks.
+template <typename T, int KB, int VB, int D>
 __global__ __launch_bounds__(256) void quant_kv_kernel(Planes p, const T* __restrict__ k,
                                                        int n_tokens, int g_begin, int g_end,
                                                        int kgx, unsigned kblocks,
                                                        const T* __restrict__ v, int n_src,
-                                                       int t_dst0, int vbx, unsigned vblocks)
+                                                       int t_dst0, int vbx)
 {
     const unsigned b = blockIdx.x;
-    const unsigned both = 2u * (kblocks < vblocks ? kblocks : vblocks);
-    bool key;
-    unsigned i;
-    if (b < both) {
-        key = (b & 1u) == 0;
-        i = b >> 1;
+    if (b < kblocks) {
+        quant_keys_block<T, KB, D>(p, k, n_tokens, g_begin, g_end, (int)(b % (unsigned)kgx),
+                                   b / (unsigned)kgx);
     } else {
-        key = kblocks > vblocks;
-        i = (both >> 1) + (b - both);
+        const unsigned i = b - kblocks;
+        quant_values_thread<T, VB, D>(p, v, n_src, n_tokens, t_dst0, (int)(i % (unsigned)vbx),
+                                      i / (unsigned)vbx);
     }
-    if (key)
-        quant_keys_block<T, KB>(p, k, n_tokens, g_begin, g_end, (int)(i % (unsigned)kgx),
-                                i / (unsigned)kgx);
-    else
-        quant_values_thread<T, VB>(p, v, n_src, n_tokens, t_dst0, (int)(i % (unsigned)vbx),
-                                   i / (unsigned)vbx);
 }
 
 // Append one token per sequence/head in one launch (block = one sequence/head,
@@ -339,6 +331,38 @@ __global__ void append_residual_kernel(Planes p, const T* __restrict__ k,
 
 // ------------------------------------------------------------- dispatch --
 
+// The key codec over channel groups [g_begin, g_end) (grid: key-group
+// blocks x sequences/heads) and the value codec over tokens [0, n_src) (rows
+// of src_stride tokens from src) into slots [t_dst0, t_dst0 + n_src), for
+// one head dimension and code width.
+template <typename T, int D>
+void launch_keys_d(const Planes& q, int bits, const T* src, int n_tokens, int g_begin, int g_end,
+                   hipStream_t stream)
+{
+    constexpr int gpb = key_groups_per_block<T>(D);
+    const dim3 grid((g_end - g_begin + gpb - 1) / gpb, q.nb * q.hkv);
+    switch (bits) {
+    case 2: quant_keys_kernel<T, 2, D><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    case 4: quant_keys_kernel<T, 4, D><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    case 8: quant_keys_kernel<T, 8, D><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
+    }
+}
+
+template <typename T, int D>
+void launch_values_d(const Planes& q, int bits, const T* src, int n_src, int src_stride,
+                     int t_dst0, hipStream_t stream)
+{
+    const int nbh = q.nb * q.hkv;  // at most 65535 sequences/heads per launch
+    for (int bh0 = 0; bh0 < nbh; bh0 += 65535) {
+        const dim3 grid(value_blocks(n_src, D), nbh - bh0 < 65535 ? nbh - bh0 : 65535);
+        switch (bits) {
+        case 2: quant_values_kernel<T, 2, D><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
+        case 4: quant_values_kernel<T, 4, D><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
+        case 8: quant_values_kernel<T, 8, D><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
+        }
+    }
+}
+
 // Channel groups [g_begin, g_end) of src into the planes `codes`/`meta`
 // (laid out [gcap][D][W]) and token groups of n_src tokens into planes laid
 // out [tcap][D/G][W]: the two quantize kernels, pointed at any plane pair.
@@ -350,33 +374,22 @@ void quantize_channel_groups(Planes q, uint32_t* codes, uint32_t* meta, int bits
         return;
     q.k_codes = codes;
     q.k_meta = meta;
-    const int gpb = key_groups_per_block<T>(q.D);
-    dim3 grid((g_end - g_begin + gpb - 1) / gpb, q.nb * q.hkv);
-    switch (bits) {
-    case 2: quant_keys_kernel<T, 2><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
-    case 4: quant_keys_kernel<T, 4><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
-    case 8: quant_keys_kernel<T, 8><<<grid, 256, 0, stream>>>(q, src, n_tokens, g_begin, g_end); break;
-    }
+    if (q.D == 128)
+        launch_keys_d<T, 128>(q, bits, src, n_tokens, g_begin, g_end, stream);
+    else
+        launch_keys_d<T, 64>(q, bits, src, n_tokens, g_begin, g_end, stream);
 }
 
-// The value codec over tokens [0, n_src) (rows of src_stride tokens from
-// src) of every sequence/head into slots [t_dst0, t_dst0 + n_src) of the
-// planes in q.v_codes / q.v_meta (at most 65535 sequences/heads per launch).
 template <typename T>
 void launch_token_groups(const Planes& q, int bits, const T* src, int n_src, int src_stride,
                          int t_dst0, hipStream_t stream)
 {
     if (n_src <= 0)
         return;
-    const int nbh = q.nb * q.hkv;
-    for (int bh0 = 0; bh0 < nbh; bh0 += 65535) {
-        const dim3 grid(value_blocks(n_src, q.D), nbh - bh0 < 65535 ? nbh - bh0 : 65535);
-        switch (bits) {
-        case 2: quant_values_kernel<T, 2><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
-        case 4: quant_values_kernel<T, 4><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
-        case 8: quant_values_kernel<T, 8><<<grid, 256, 0, stream>>>(q, src, n_src, src_stride, t_dst0, (size_t)bh0); break;
-        }
-    }
+    if (q.D == 128)
+        launch_values_d<T, 128>(q, bits, src, n_src, src_stride, t_dst0, stream);
+    else
+        launch_values_d<T, 64>(q, bits, src, n_src, src_stride, t_dst0, stream);
 }
 
 template <typename T>
@@ -421,6 +434,29 @@ hipError_t quantize_prefill_geometry(const Planes& p, const T* k, const T* v, in
     return hipGetLastError();
 }
 
+template <typename T, int D>
+void launch_kv_d(const Planes& p, const T* k, int n_tokens, int g_begin, int g_end, int kgx,
+                 unsigned kblocks, const T* vsrc, int n_src, int t_dst0, int vbx,
+                 unsigned vblocks, hipStream_t stream)
+{
+    const unsigned blocks = kblocks + vblocks;
+#define KVQ_KV(KBB, VBB)                                                                 \
+    quant_kv_kernel<T, KBB, VBB, D><<<blocks, 256, 0, stream>>>(                         \
+        p, k, n_tokens, g_begin, g_end, kgx, kblocks, vsrc, n_src, t_dst0, vbx)
+    switch (p.kbits * 16 + p.vbits) {
+    case 2 * 16 + 2: KVQ_KV(2, 2); break;
+    case 2 * 16 + 4: KVQ_KV(2, 4); break;
+    case 2 * 16 + 8: KVQ_KV(2, 8); break;
+    case 4 * 16 + 2: KVQ_KV(4, 2); break;
+    case 4 * 16 + 4: KVQ_KV(4, 4); break;
+    case 4 * 16 + 8: KVQ_KV(4, 8); break;
+    case 8 * 16 + 2: KVQ_KV(8, 2); break;
+    case 8 * 16 + 4: KVQ_KV(8, 4); break;
+    case 8 * 16 + 8: KVQ_KV(8, 8); break;
+    }
+#undef KVQ_KV
+}
+
 template <typename T>
 hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tokens,
                               hipStream_t stream)
@@ -445,31 +481,16 @@ hipError_t quantize_prefill_t(const Planes& p, const T* k, const T* v, int n_tok
     bool values_done = false;
     if (kblocks > 0 && vblocks > 0 && kblocks + vblocks <= (size_t)UINT32_MAX) {
         // both codecs in one launch
-        const unsigned blocks = (unsigned)(kblocks + vblocks);
-#define KVQ_KV(KBB, VBB)                                                                     \
-    quant_kv_kernel<T, KBB, VBB><<<blocks, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end, \
-                                                             kgx, (unsigned)kblocks, vsrc,     \
-                                                             vq - v0, v0, vbx, (unsigned)vblocks)
-        switch (p.kbits * 16 + p.vbits) {
-        case 2 * 16 + 2: KVQ_KV(2, 2); break;
-        case 2 * 16 + 4: KVQ_KV(2, 4); break;
-        case 2 * 16 + 8: KVQ_KV(2, 8); break;
-        case 4 * 16 + 2: KVQ_KV(4, 2); break;
-        case 4 * 16 + 4: KVQ_KV(4, 4); break;
-        case 4 * 16 + 8: KVQ_KV(4, 8); break;
-        case 8 * 16 + 2: KVQ_KV(8, 2); break;
-        case 8 * 16 + 4: KVQ_KV(8, 4); break;
-        case 8 * 16 + 8: KVQ_KV(8, 8); break;
-        }
-#undef KVQ_KV
+        if (p.D == 128)
+            launch_kv_d<T, 128>(p, k, n_tokens, g_begin, g_end, kgx, (unsigned)kblocks, vsrc,
+                                vq - v0, v0, vbx, (unsigned)vblocks, stream);
+        else
+            launch_kv_d<T, 64>(p, k, n_tokens, g_begin, g_end, kgx, (unsigned)kblocks, vsrc,
+                               vq - v0, v0, vbx, (unsigned)vblocks, stream);
         values_done = true;
     } else if (kblocks > 0) {
-        dim3 grid(kgx, nbh);
-        switch (p.kbits) {
-        case 2: quant_keys_kernel<T, 2><<<grid, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
-        case 4: quant_keys_kernel<T, 4><<<grid, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
-        case 8: quant_keys_kernel<T, 8><<<grid, 256, 0, stream>>>(p, k, n_tokens, g_begin, g_end); break;
-        }
+        quantize_channel_groups<T>(p, p.k_codes, p.k_meta, p.kbits, k, n_tokens, g_begin, g_end,
+                                   stream);
     }
     auto copy = [&](const T* src, void* dst, int slots, int t0, int t1) {
         const size_t total = (size_t)nbh * (t1 - t0) * p.D;
