@@ -35,6 +35,11 @@
  *   - Every function returns KVQ_OK (0) or a negative KVQ_ERR_* code.  All
  *     argument and state checks run before anything is enqueued: on error the
  *     handle's state is unchanged and no GPU work was queued.
+ *   - Debugging: with the environment variable KVQ_SYNC set to 1 when a
+ *     handle is created, every call on that handle that enqueues work then
+ *     synchronizes its stream and checks the runtime's error state, so a
+ *     kernel fault is reported (KVQ_ERR_HIP, handle state not advanced) by
+ *     the call that caused it.  Not for use under stream capture.
  *   - Element types (kvq_config.dtype): KVQ_F16 (IEEE binary16) or KVQ_F32.
  *     Keys, values, queries and the key tail use that type; the output is
  *     always fp32.  Non-finite inputs are undefined behaviour.

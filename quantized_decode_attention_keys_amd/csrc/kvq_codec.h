@@ -223,7 +223,9 @@ KVQ_HD uint32_t quantize_group(const float (&x)[32], uint32_t (&w)[BITS])
 // [0, (2^B - 1)(1 + 2^-11)], below 2^B - 1/2; a zero or subnormal step
 // (rounded by up to half of itself) sends the group down the exact path.
 
+#if defined(__HIP_DEVICE_COMPILE__)
 typedef _Float16 kvq_h2 __attribute__((ext_vector_type(2)));
+#endif
 
 // Low and high binary16 values of a packed word, as floats (exact).
 KVQ_HD float h16_lo(uint32_t d)

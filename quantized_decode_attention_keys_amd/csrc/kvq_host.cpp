@@ -17,6 +17,7 @@ struct kvq {
     int32_t cus;            // compute units of the device the handle was made on
     int32_t force_splits;   // tuning overrides (KVQ_ATTEND_SPLITS / KVQ_ATTEND_WAVES), 0 = auto
     int32_t force_waves;
+    int32_t sync;           // KVQ_SYNC=1: each call waits for its work and checks for a fault
     float* scratch;         // the library's static device scratch on the handle's device
 };
 
@@ -134,6 +135,20 @@ int env_int(const char* name)
 {
     const char* v = std::getenv(name);
     return v ? std::atoi(v) : 0;
+}
+
+// The status of a call that enqueued work with status st: in debug-sync mode
+// the stream is drained and the runtime's error state read, so a fault in
+// that work is reported here.
+int settle(const kvq* h, void* stream, int st)
+{
+    if (st != KVQ_OK || !h->sync)
+        return st;
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    const hipError_t last = hipGetLastError();
+    if (e == hipSuccess)
+        e = last;
+    return hip_status(e);
 }
 
 // Launch shape of the decode-attention kernel.  A compute unit holds about
@@ -273,10 +288,12 @@ int append_attend(kvq* h, const void* d_k, const void* d_v, const void* d_q, flo
     if (!fused) {
         const int st = kvq_append_token(h, d_k, d_v, stream);
         return st != KVQ_OK ? st
-                            : launch_attend(h, n, splits, waves, d_q, d_out, nullptr, nullptr, s,
-                                            use_static);
+                            : settle(h, stream,
+                                     launch_attend(h, n, splits, waves, d_q, d_out, nullptr,
+                                                   nullptr, s, use_static));
     }
-    const int st = launch_attend(h, n, splits, waves, d_q, d_out, d_k, d_v, s, use_static);
+    const int st =
+        settle(h, stream, launch_attend(h, n, splits, waves, d_q, d_out, d_k, d_v, s, use_static));
     if (st == KVQ_OK)
         h->n = n;
     return st;
@@ -361,6 +378,7 @@ int kvq_create(const kvq_config* cfg, void* d_ws, size_t ws_bytes, kvq_t** out)
         h->cus = prop.multiProcessorCount;
     h->force_splits = env_int("KVQ_ATTEND_SPLITS");
     h->force_waves = env_int("KVQ_ATTEND_WAVES");
+    h->sync = env_int("KVQ_SYNC") == 1;
     *out = h;
     return KVQ_OK;
 }
@@ -380,9 +398,10 @@ int kvq_quantize_prefill(kvq_t* h, const void* d_k, const void* d_v, int32_t n_t
         return KVQ_OK;
     const kvqi::Planes p = planes_of(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int st = hip_status(p.format == kvqi::kFormatFp8
-                                  ? kvqi::launch_fp8_prefill(p, d_k, d_v, n_tokens, s)
-                                  : kvqi::launch_quantize_prefill(p, d_k, d_v, n_tokens, s));
+    const int st = settle(h, stream,
+                          hip_status(p.format == kvqi::kFormatFp8
+                                         ? kvqi::launch_fp8_prefill(p, d_k, d_v, n_tokens, s)
+                                         : kvqi::launch_quantize_prefill(p, d_k, d_v, n_tokens, s)));
     if (st == KVQ_OK)
         h->n = n_tokens;
     return st;
@@ -396,9 +415,10 @@ int kvq_append_token(kvq_t* h, const void* d_k, const void* d_v, void* stream)
         return KVQ_ERR_CAPACITY;
     const kvqi::Planes p = planes_of(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int st = hip_status(p.format == kvqi::kFormatFp8
-                                  ? kvqi::launch_fp8_append(p, d_k, d_v, h->n, s)
-                                  : kvqi::launch_append(p, d_k, d_v, h->n, s));
+    const int st = settle(h, stream,
+                          hip_status(p.format == kvqi::kFormatFp8
+                                         ? kvqi::launch_fp8_append(p, d_k, d_v, h->n, s)
+                                         : kvqi::launch_append(p, d_k, d_v, h->n, s)));
     if (st == KVQ_OK)
         h->n += 1;
     return st;
@@ -412,8 +432,9 @@ int kvq_attend_decode(kvq_t* h, const void* d_q, float* d_out, void* stream)
         return KVQ_ERR_STATE;
     int splits, waves;
     plan_attend(h, h->n, false, &splits, &waves);
-    return launch_attend(h, h->n, splits, waves, d_q, d_out, nullptr, nullptr,
-                         static_cast<hipStream_t>(stream), false);
+    return settle(h, stream,
+                  launch_attend(h, h->n, splits, waves, d_q, d_out, nullptr, nullptr,
+                                static_cast<hipStream_t>(stream), false));
 }
 
 int kvq_append_attend(kvq_t* h, const void* d_k, const void* d_v, const void* d_q,
@@ -437,8 +458,9 @@ int kvq_error_metrics(kvq_t* h, const void* d_k, const void* d_v, const void* d_
         return KVQ_ERR_STATE;
     if (h->cfg.format != KVQ_FORMAT_INT)
         return KVQ_ERR_UNSUPPORTED;
-    return hip_status(kvqi::launch_error_metrics(planes_of(h), d_k, d_v, d_q, d_metrics, h->n,
-                                                 static_cast<hipStream_t>(stream)));
+    return settle(h, stream,
+                  hip_status(kvqi::launch_error_metrics(planes_of(h), d_k, d_v, d_q, d_metrics,
+                                                        h->n, static_cast<hipStream_t>(stream))));
 }
 
 int kvq_destroy(kvq_t* h)
