@@ -139,6 +139,23 @@ __device__ __forceinline__ half2v pack_h2(float lo, float hi)
     return r;
 }
 
+// Operands of v_mfma_f32_16x16x32_f16: eight binary16 values per lane.
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// (a, b) as two binary16 pairs hi + lo: hi rounded toward zero, lo the
+// remainder (exact in fp32) rounded toward zero, so a = hi.x + lo.x within
+// 2^-20 |a| or 2^-24, whichever is larger (b likewise).  Products of such
+// splits summed as hi*hi + hi*lo + lo*hi carry fp32-class accuracy through
+// a binary16 matrix instruction (lo*lo, below 2^-20 of the product, is left
+// out).
+__device__ __forceinline__ uint2 split_h2(float a, float b)
+{
+    const auto hi = __builtin_amdgcn_cvt_pkrtz(a, b);
+    const auto lo = __builtin_amdgcn_cvt_pkrtz(a - (float)hi[0], b - (float)hi[1]);
+    return make_uint2(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo));
+}
+
 // Value of v in another lane of the same 16-lane row (DPP, VALU only).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
@@ -671,7 +688,9 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     using VC = Codec<VB>;
     constexpr int NP = S::NP;
     constexpr int RS = S::RED_STRIDE;
-    extern __shared__ float smem[];  // [nwaves][64][RS] reduce buffers, reused for the merge
+    // [nwaves][64][RS] reduce buffers, reused for the merge; 16-byte aligned
+    // for the 16-byte operand reads of the matrix-core scores
+    extern __shared__ __attribute__((aligned(16))) float smem[];
 
     const int nwaves = blockDim.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -709,6 +728,12 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     hp.vm = p.v_meta + bh * (size_t)p.tcap * S::NCG;
     const int stride = nwaves * S::GPW;
     constexpr bool kDynamicGroups = dynamic_groups(QPK);
+    // Several query heads and head_dim 128: the heads' scores on the matrix
+    // cores (one lane per channel pair, a whole group per wave step).
+    constexpr bool kMfmaHeads = QPK > 1 && NP == 64;
+    constexpr int kUS = 68;  // words per row of the MFMA operand staging
+    static_assert(!kMfmaHeads || (32 + 2 * QPK) * kUS <= S::NRED * 64 * RS,
+                  "operand staging inside the wave's reduce buffers");
     StepData<KB, S::NVW, S::NVM> cur, nxt;
     int gb = g0 + wave * S::GPW;
     if (appends && threadIdx.x < D) {  // whole waves: D is a multiple of 64
@@ -902,10 +927,15 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
             // each (pair, token) once, U_j = T_j (x + i y) (times the field
             // scale 2^(pos-24) and its inverse folded into T_j), then each
             // head's term is Re[Q_h U_j] with Q_h = conj(q'_h) e^{i g G theta_i}.
+            // With the matrix-core scores, U is formed at 1/4 scale (folded
+            // into the dequantization) so that it fits binary16 for any
+            // binary16 keys; the queries carry the factor 4.
+            constexpr float kUScale = kMfmaHeads ? 0.25f : 1.0f;
+            const float s0u = s0 * kUScale, s1u = s1 * kUScale;
             float z0s[KC::NSCALE], z1s[KC::NSCALE];
 #pragma unroll
             for (int k = 0; k < KC::NSCALE; ++k) {
-                const float sc = 1.0f / (float)(1 << (24 - k * KB));
+                const float sc = kUScale / (float)(1 << (24 - k * KB));
                 z0s[k] = z0 * sc;
                 z1s[k] = z1 * sc;
             }
@@ -923,32 +953,118 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                         const int jj = w * 2 * KC::TPH + half * KC::TPH + f;
                         const float c0 = half ? hi_h(m0) : lo_h(m0);
                         const float c1 = half ? hi_h(m1) : lo_h(m1);
-                        const float x = fmaf(s0, c0, z0s[sidx]);
-                        const float y = fmaf(s1, c1, z1s[sidx]);
+                        const float x = fmaf(s0u, c0, z0s[sidx]);
+                        const float y = fmaf(s1u, c1, z1s[sidx]);
                         const float2 tw = twiddle(jj);  // (T.x, -T.y) * 2^(24-pos)
                         ux[jj] = fmaf(tw.x, x, tw.y * y);
                         uy[jj] = fmaf(tw.x, y, -(tw.y * x));
                     }
                 }
             }
+            if constexpr (kMfmaHeads) {
+                // The heads' scores of the step's 32 tokens as one matrix
+                // product on the matrix cores: S[h][j] = sum_k A[h][k] B[k][j]
+                // over k = 2 i + {0, 1} for the 64 pairs, A[h][2i] = 4 Q_h.x,
+                // A[h][2i+1] = -4 Q_h.y, B[2i][j] = U_j.x / 4, B[2i+1][j] =
+                // U_j.y / 4 (both inside binary16 for any binary16 inputs).
+                // Every operand is split hi + lo (split_h2) and hi*hi + hi*lo
+                // + lo*hi accumulate in fp32 in v_mfma_f32_16x16x32_f16.  The
+                // operands reach the MFMA lane layouts through this wave's
+                // region of the reduce buffers: lane i (pair i) writes one
+                // (hi, lo) word pair per head and per token, and each lane
+                // reads 16-byte runs of four pairs (rows padded to kUS words,
+                // so the column reads of 16 lanes hit distinct banks).  All
+                // of it stays inside the wave, whose LDS accesses execute in
+                // program order; the compiler barriers keep that order.
+                uint32_t* const wsb = reinterpret_cast<uint32_t*>(red);
+                uint32_t* const uhi = wsb;             // [16 tokens][kUS]
+                uint32_t* const ulo = wsb + 16 * kUS;
+                uint32_t* const qhi = wsb + 32 * kUS;  // [QPK heads][kUS]
+                uint32_t* const qlo = qhi + QPK * kUS;
 #pragma unroll
-            for (int h = 0; h < QPK; ++h) {
-                // heads alternate between two buffers, so one head's writes
-                // need not wait for the previous head's reads
-                float* rb = red + (S::NRED > 1 ? (h & 1) : 0) * 64 * RS;
-                const float2 Q = cmul(qc[h], use.rg);
-                const float nqy = -Q.y;
+                for (int h = 0; h < QPK; ++h) {
+                    const float2 Q = cmul(qc[h], use.rg);
+                    const uint2 w = split_h2(4.0f * Q.x, -4.0f * Q.y);
+                    qhi[h * kUS + i] = w.x;
+                    qlo[h * kUS + i] = w.y;
+                }
+                auto store_tile = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-                for (int jj = 0; jj < G; ++jj)
-                    rb[lane * RS + jj] = fmaf(Q.x, ux[jj], nqy * uy[jj]);
-                float a4[4] = {0.f, 0.f, 0.f, 0.f};
+                    for (int jj = 0; jj < 16; ++jj) {
+                        const uint2 w = split_h2(ux[16 * t + jj], uy[16 * t + jj]);
+                        uhi[jj * kUS + i] = w.x;
+                        ulo[jj * kUS + i] = w.y;
+                    }
+                };
+                store_tile(0);
+                asm volatile("" ::: "memory");
+                // A: lane (row m = lane % 16, k-run kq = lane / 16); rows
+                // past the heads are zero.  B: lane (token column m, kq).
+                const int mrow = lane & 15, kq = lane >> 4;
+                half8v ahi[4], alo[4];
 #pragma unroll
-                for (int m = 0; m < 32; ++m)
-                    a4[m & 3] += rb[(red_half + m) * RS + red_col];
-                float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-                if (NP == 64)
-                    acc = half_sum(acc);
-                s[h] = acc;
+                for (int sk = 0; sk < 4; ++sk) {
+                    ahi[sk] = half8v{};
+                    alo[sk] = half8v{};
+                    if (mrow < QPK) {
+                        ahi[sk] = *reinterpret_cast<const half8v*>(qhi + mrow * kUS + 16 * sk + 4 * kq);
+                        alo[sk] = *reinterpret_cast<const half8v*>(qlo + mrow * kUS + 16 * sk + 4 * kq);
+                    }
+                }
+                float4v acc[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    if (t == 1) {
+                        asm volatile("" ::: "memory");
+                        store_tile(1);
+                        asm volatile("" ::: "memory");
+                    }
+                    float4v c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int sk = 0; sk < 4; ++sk) {
+                        const half8v bhi =
+                            *reinterpret_cast<const half8v*>(uhi + mrow * kUS + 16 * sk + 4 * kq);
+                        const half8v blo =
+                            *reinterpret_cast<const half8v*>(ulo + mrow * kUS + 16 * sk + 4 * kq);
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[sk], bhi, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[sk], blo, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[sk], bhi, c, 0, 0, 0);
+                    }
+                    acc[t] = c;
+                }
+                asm volatile("" ::: "memory");
+                // Lanes 0..15 hold the heads of token `lane` in acc[0] and of
+                // token 16 + lane in acc[1]; the softmax wants token lane % 32
+                // in lane: row 1 takes row 0's acc[1], rows 2 and 3 rows 0, 1.
+                // (Both swaps run in every lane: inside a branch, the lanes
+                // they read from would be inactive.)
+                const bool row1 = (lane & 16) != 0;
+#pragma unroll
+                for (int h = 0; h < QPK; ++h) {
+                    const float from_row0 = swap16(acc[1][h]).a;
+                    const float x = row1 ? from_row0 : acc[0][h];
+                    s[h] = swap32(x).a;
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < QPK; ++h) {
+                    // heads alternate between two buffers, so one head's writes
+                    // need not wait for the previous head's reads
+                    float* rb = red + (S::NRED > 1 ? (h & 1) : 0) * 64 * RS;
+                    const float2 Q = cmul(qc[h], use.rg);
+                    const float nqy = -Q.y;
+#pragma unroll
+                    for (int jj = 0; jj < G; ++jj)
+                        rb[lane * RS + jj] = fmaf(Q.x, ux[jj], nqy * uy[jj]);
+                    float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < 32; ++m)
+                        a4[m & 3] += rb[(red_half + m) * RS + red_col];
+                    float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+                    if (NP == 64)
+                        acc = half_sum(acc);
+                    s[h] = acc;
+                }
             }
         }
         if constexpr (kDefer) {
