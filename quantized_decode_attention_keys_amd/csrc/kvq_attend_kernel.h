@@ -148,12 +148,16 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 // 2^-20 |a| or 2^-24, whichever is larger (b likewise).  Products of such
 // splits summed as hi*hi + hi*lo + lo*hi carry fp32-class accuracy through
 // a binary16 matrix instruction (lo*lo, below 2^-20 of the product, is left
-// out).
-__device__ __forceinline__ uint2 split_h2(float a, float b)
+// out).  m1 is -1.0 held where the compiler cannot see its value: the
+// remainders a - hi.x = hi.x * m1 + a then stay one v_fma_mix_f32 each,
+// reading the binary16 half in place (a - hi.x would convert, then
+// subtract).
+__device__ __forceinline__ uint2 split_h2(float a, float b, float m1)
 {
     const auto hi = __builtin_amdgcn_cvt_pkrtz(a, b);
-    const auto lo = __builtin_amdgcn_cvt_pkrtz(a - (float)hi[0], b - (float)hi[1]);
-    return make_uint2(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo));
+    const float ra = fmaf((float)hi[0], m1, a), rb = fmaf((float)hi[1], m1, b);
+    return make_uint2(__builtin_bit_cast(uint32_t, hi),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ra, rb)));
 }
 
 // Value of v in another lane of the same 16-lane row (DPP, VALU only).
@@ -981,17 +985,19 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 uint32_t* const ulo = wsb + 16 * kUS;
                 uint32_t* const qhi = wsb + 32 * kUS;  // [QPK heads][kUS]
                 uint32_t* const qlo = qhi + QPK * kUS;
+                float m1 = -1.0f;
+                asm volatile("" : "+v"(m1));
 #pragma unroll
                 for (int h = 0; h < QPK; ++h) {
                     const float2 Q = cmul(qc[h], use.rg);
-                    const uint2 w = split_h2(4.0f * Q.x, -4.0f * Q.y);
+                    const uint2 w = split_h2(4.0f * Q.x, -4.0f * Q.y, m1);
                     qhi[h * kUS + i] = w.x;
                     qlo[h * kUS + i] = w.y;
                 }
                 auto store_tile = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
                     for (int jj = 0; jj < 16; ++jj) {
-                        const uint2 w = split_h2(ux[16 * t + jj], uy[16 * t + jj]);
+                        const uint2 w = split_h2(ux[16 * t + jj], uy[16 * t + jj], m1);
                         uhi[jj * kUS + i] = w.x;
                         ulo[jj * kUS + i] = w.y;
                     }
