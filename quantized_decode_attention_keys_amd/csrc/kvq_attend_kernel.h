@@ -735,7 +735,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     // Several query heads and head_dim 128: the heads' scores on the matrix
     // cores (one lane per channel pair, a whole group per wave step).
     constexpr bool kMfmaHeads = QPK > 1 && NP == 64;
-    constexpr int kUS = 68;  // words per row of the MFMA operand staging
+    constexpr int kUS = 64;  // words per row of the MFMA operand staging
     static_assert(!kMfmaHeads || (32 + 2 * QPK) * kUS <= S::NRED * 64 * RS,
                   "operand staging inside the wave's reduce buffers");
     StepData<KB, S::NVW, S::NVM> cur, nxt;
@@ -976,8 +976,8 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 // operands reach the MFMA lane layouts through this wave's
                 // region of the reduce buffers: lane i (pair i) writes one
                 // (hi, lo) word pair per head and per token, and each lane
-                // reads 16-byte runs of four pairs (rows padded to kUS words,
-                // so the column reads of 16 lanes hit distinct banks).  All
+                // reads 16-byte runs of four pairs (16-byte chunks swizzled
+                // by row, so the column reads hit distinct banks).  All
                 // of it stays inside the wave, whose LDS accesses execute in
                 // program order; the compiler barriers keep that order.
                 uint32_t* const wsb = reinterpret_cast<uint32_t*>(red);
@@ -985,21 +985,24 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 uint32_t* const ulo = wsb + 16 * kUS;
                 uint32_t* const qhi = wsb + 32 * kUS;  // [QPK heads][kUS]
                 uint32_t* const qlo = qhi + QPK * kUS;
+                // word c of a row at 16-byte chunk (c / 4) XOR (row % 16):
+                // the 16-byte reads of a column of rows fall in distinct banks
+                auto swz = [](int row, int c) { return (((c >> 2) ^ (row & 15)) << 2) | (c & 3); };
                 float m1 = -1.0f;
                 asm volatile("" : "+v"(m1));
 #pragma unroll
                 for (int h = 0; h < QPK; ++h) {
                     const float2 Q = cmul(qc[h], use.rg);
                     const uint2 w = split_h2(4.0f * Q.x, -4.0f * Q.y, m1);
-                    qhi[h * kUS + i] = w.x;
-                    qlo[h * kUS + i] = w.y;
+                    qhi[h * kUS + swz(h, i)] = w.x;
+                    qlo[h * kUS + swz(h, i)] = w.y;
                 }
                 auto store_tile = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
                     for (int jj = 0; jj < 16; ++jj) {
                         const uint2 w = split_h2(ux[16 * t + jj], uy[16 * t + jj], m1);
-                        uhi[jj * kUS + i] = w.x;
-                        ulo[jj * kUS + i] = w.y;
+                        uhi[jj * kUS + swz(jj, i)] = w.x;
+                        ulo[jj * kUS + swz(jj, i)] = w.y;
                     }
                 };
                 store_tile(0);
@@ -1013,8 +1016,8 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                     ahi[sk] = half8v{};
                     alo[sk] = half8v{};
                     if (mrow < QPK) {
-                        ahi[sk] = *reinterpret_cast<const half8v*>(qhi + mrow * kUS + 16 * sk + 4 * kq);
-                        alo[sk] = *reinterpret_cast<const half8v*>(qlo + mrow * kUS + 16 * sk + 4 * kq);
+                        ahi[sk] = *reinterpret_cast<const half8v*>(qhi + mrow * kUS + swz(mrow, 16 * sk + 4 * kq));
+                        alo[sk] = *reinterpret_cast<const half8v*>(qlo + mrow * kUS + swz(mrow, 16 * sk + 4 * kq));
                     }
                 }
                 float4v acc[2];
@@ -1029,9 +1032,9 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
 #pragma unroll
                     for (int sk = 0; sk < 4; ++sk) {
                         const half8v bhi =
-                            *reinterpret_cast<const half8v*>(uhi + mrow * kUS + 16 * sk + 4 * kq);
+                            *reinterpret_cast<const half8v*>(uhi + mrow * kUS + swz(mrow, 16 * sk + 4 * kq));
                         const half8v blo =
-                            *reinterpret_cast<const half8v*>(ulo + mrow * kUS + 16 * sk + 4 * kq);
+                            *reinterpret_cast<const half8v*>(ulo + mrow * kUS + swz(mrow, 16 * sk + 4 * kq));
                         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[sk], bhi, c, 0, 0, 0);
                         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[sk], blo, c, 0, 0, 0);
                         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[sk], bhi, c, 0, 0, 0);
