@@ -406,23 +406,15 @@ def fp8_encode(x: float) -> int:
     return lib().orc_fp8_encode(float(x))
 
 
-def fp8_view(planes: np.ndarray) -> np.ndarray:
-    """Logical [nb][Hkv][Gcap][D][32] view (channel, token in group) of FP8
-    planes uint8[nb][Hkv][Gcap][2][2][D/2][16] (channel parity, token half,
-    channel pair, token mod 16)."""
-    nb, hkv, gcap, _, _, np2, _ = planes.shape
-    x = planes.transpose(0, 1, 2, 5, 3, 4, 6)        # nb hkv g pair parity half byte
-    return x.reshape(nb, hkv, gcap, 2 * np2, 32)
-
-
 def quantize_fp8(x: np.ndarray, G: int = 32, max_tokens=None) -> np.ndarray:
-    """FP8 E4M3 planes uint8[nb][Hkv][Gcap][2][2][D/2][16] of x[nb][Hkv][T][D]:
-    channel c, token j of a group at [c % 2][j / 16][c / 2][j % 16]."""
+    """FP8 E4M3 planes uint8[nb][Hkv][Gcap][D][32] of x[nb][Hkv][T][D]:
+    channel c, token j of group g at [g][c][j] (bytes of a group past T are
+    0)."""
     x = np.ascontiguousarray(x)
     nb, hkv, T, D = x.shape
     cap = T if max_tokens is None else max_tokens
     gcap = -(-max(cap, 1) // G)
-    out = np.zeros((nb, hkv, gcap, 2, 2, D // 2, 16), dtype=np.uint8)
+    out = np.zeros((nb, hkv, gcap, D, G), dtype=np.uint8)
     if lib().orc_quantize_fp8(_ptr(x), _dtype_code(x), nb, hkv, T, D, G, gcap, _ptr(out)) != 0:
         raise ValueError("orc_quantize_fp8 failed")
     return out

@@ -57,12 +57,11 @@
  *      3 mantissa bits; largest finite 448; no infinities).  Readings: no
  *      scale factor (scale 1); round to nearest, ties to even, values beyond
  *      the largest finite saturate to +-448; keys stored before the rotary
- *      embedding like the integer cache; inside each 32-token group the
- *      bytes of channel c, token j sit at
- *        ((2 * (c % 2) + j / 16) * (D / 2) + c / 2) * 16 + j % 16
- *      of a D * 32-byte block ([nb][Hkv][Gcap][D * 32]): 16-byte pieces, so
- *      the reader that owns channel pair c/2 finds its four pieces at a
- *      stride of D * 8 bytes.
+ *      embedding like the integer cache.  Planes here are in the logical
+ *      order [nb][Hkv][Gcap][D][32]: inside each 32-token group the byte of
+ *      channel c, token j sits at c * 32 + j.  (The pages fix no byte order;
+ *      the GPU library keeps the same bytes in an order of its own, and the
+ *      tests permute its planes to this one before comparing.)
  *   6. Geometry ablation ([BITS], lede and "Keys: The Outliers Live in Fixed
  *      Channels", "Values: Where the Intuition Breaks"): the same 2 bits
  *      spent along the other axis -- keys per token (a group is G channels
@@ -785,10 +784,11 @@ uint8_t orc_fp8_encode(double x)
     return sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8));
 }
 
-/* Byte of token j (< 32), channel c inside a group block of D * 32 bytes. */
-static size_t fp8_offset(int D, int c, int j)
+/* Byte of token j (< 32), channel c inside a group block of D * 32 bytes:
+ * the logical, channel-major order. */
+static size_t fp8_offset(int c, int j)
 {
-    return ((size_t)(2 * (c % 2) + j / 16) * (D / 2) + c / 2) * 16 + j % 16;
+    return (size_t)c * 32 + (size_t)j;
 }
 
 /* FP8 planes for T tokens of x[nb][Hkv][T][D] (keys or values), group g of
@@ -807,7 +807,7 @@ int orc_quantize_fp8(const void* x, int dtype, int nb, int hkv, int T, int D,
                 for (int c = 0; c < D; ++c)
                     for (int j = 0; j < G; ++j) {
                         int t = g * G + j;
-                        size_t o = (bh * gcap + g) * D * G + fp8_offset(D, c, j);
+                        size_t o = (bh * gcap + g) * D * G + fp8_offset(c, j);
                         planes[o] = t < T ? orc_fp8_encode(load_elem(
                                                 x, dtype, (bh * T + t) * D + c))
                                           : 0;
@@ -844,7 +844,7 @@ int orc_attend_fp8(int nb, int hq, int hkv, int D, int G, int gcap, double base,
         orc_rope(qr, D, (double)(n - 1), base);
         for (int t = 0; t < n; ++t) {
             for (int c = 0; c < D; ++c) {
-                size_t o = (bh * gcap + t / G) * D * G + fp8_offset(D, c, t % G);
+                size_t o = (bh * gcap + t / G) * D * G + fp8_offset(c, t % G);
                 kr[c] = orc_fp8_decode(k8[o]);
                 vals[(size_t)t * D + c] = orc_fp8_decode(v8[o]);
             }

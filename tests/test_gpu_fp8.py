@@ -8,6 +8,7 @@ import torch
 
 import oracle
 import synth
+from fp8_layout import to_logical
 from _parity import TOL, _TORCH, assert_attention_close, dev, to_gpu
 from quantized_decode_attention_keys_amd import (KVQ_FORMAT_FP8_E4M3, KvqError,
                                                  QuantizedKVCache)
@@ -24,8 +25,9 @@ def make_cache(cfg, cap):
 
 
 def planes(cache):
+    """The cache's FP8 planes in the oracle's [group][channel][token] order."""
     torch.cuda.synchronize()
-    return {k: t.cpu().numpy() for k, t in cache.planes().items()}
+    return {k: to_logical(t.cpu().numpy()) for k, t in cache.planes().items()}
 
 
 def assert_bytes_equal(gp, k, v, n, cap, seqs=None):

@@ -1,8 +1,9 @@
 """Pins for the oracle's FP8 (OCP E4M3) cache ("Rotate, Then Round: The
 Geometry of KV-Cache Compression", key takeaways: FP8 as the production
 default).  Readings: round to nearest, ties to even, saturation at +-448,
-no scale factor, bytes of a 32-token group in 16-byte pieces (channel
-parity, token half, channel pair, token mod 16).
+no scale factor, the oracle's planes in the logical order (group, channel,
+token in group); the GPU library's 16-byte piece order is a permutation of
+it that the tests undo (tests/fp8_layout.py).
 
 The format is checked against its definition (closed-form values of named
 codes, symmetry, ordering), the encoder by brute force over every finite
@@ -12,6 +13,8 @@ byte with that brute-force encoder, attention against the dense formula on
 the decoded tensors."""
 import numpy as np
 import pytest
+
+from fp8_layout import piece_offset, to_logical
 
 D = 64
 G = 32
@@ -89,30 +92,37 @@ def test_round_trip_error_bound(orc):
 
 @pytest.mark.parametrize("T", [1, 31, 32, 77])
 def test_planes_layout(orc, T):
-    """Byte of token t = 32g + j, channel c at offset
-    ((2 (c mod 2) + j div 16) (D/2) + c div 2) 16 + j mod 16 of group block g,
-    checked on the flat bytes."""
+    """Byte of token t = 32g + j, channel c at offset 32 c + j of group block
+    g (the logical order), checked on the flat bytes; bytes past T are 0."""
     rng = np.random.default_rng(T)
     x = (rng.standard_normal((2, 3, T, D)) * 20).astype(np.float16)
     pl = orc.quantize_fp8(x, max_tokens=96)
-    assert pl.shape == (2, 3, 3, 2, 2, D // 2, 16)
+    assert pl.shape == (2, 3, 3, D, G)
     flat = pl.reshape(2, 3, 3, D * G)
     table = _table(orc)
     c = np.arange(D)
     for t in range(-(-T // G) * G):
-        j = t % G
-        off = ((2 * (c % 2) + j // 16) * (D // 2) + c // 2) * 16 + j % 16
-        got = flat[:, :, t // G][:, :, off]
+        got = flat[:, :, t // G][:, :, 32 * c + t % G]
         if t < T:
             want = _brute_encode(x[:, :, t].astype(np.float64).ravel(), table).reshape(2, 3, D)
             assert np.array_equal(got, want)
         else:
             assert not got.any()
-    # the logical view reads the same bytes
-    view = orc.fp8_view(pl)
-    for t in range(T):
-        assert np.array_equal(view[:, :, t // G, :, t % G], flat[:, :, t // G][
-            :, :, ((2 * (c % 2) + (t % G) // 16) * (D // 2) + c // 2) * 16 + t % 16])
+
+
+def test_gpu_piece_permutation():
+    """The tests' map from the GPU library's piece order to the logical one
+    moves the byte at the documented piece offset of (c, j) to [c][j]."""
+    rng = np.random.default_rng(5)
+    pieces = rng.integers(0, 256, (2, 3, 2, 2, 2, D // 2, 16), dtype=np.uint8)
+    flat = pieces.reshape(2, 3, 2, D * G)
+    logical = to_logical(pieces)
+    assert logical.shape == (2, 3, 2, D, G)
+    offs = [piece_offset(D, c, j) for c in range(D) for j in range(G)]
+    assert sorted(offs) == list(range(D * G))      # a permutation of the block
+    for c in range(D):
+        for j in range(G):
+            assert np.array_equal(logical[:, :, :, c, j], flat[:, :, :, piece_offset(D, c, j)])
 
 
 @pytest.mark.parametrize("n", [1, 33, 100])
@@ -125,8 +135,7 @@ def test_attention_equals_dense_on_decoded(orc, n):
     k8, v8 = orc.quantize_fp8(k, max_tokens=128), orc.quantize_fp8(v, max_tokens=128)
     out = orc.attend_fp8(k8, v8, q, n, hkv=2)
     dec = np.vectorize(orc.fp8_decode)
-    kv, vv = orc.fp8_view(k8), orc.fp8_view(v8)
-    kd = np.stack([dec(kv[:, :, t // G, :, t % G]) for t in range(n)], axis=2)
-    vd = np.stack([dec(vv[:, :, t // G, :, t % G]) for t in range(n)], axis=2)
+    kd = np.stack([dec(k8[:, :, t // G, :, t % G]) for t in range(n)], axis=2)
+    vd = np.stack([dec(v8[:, :, t // G, :, t % G]) for t in range(n)], axis=2)
     dense = orc.attend_dense(kd.astype(np.float32), vd.astype(np.float32), q.astype(np.float32))
     assert np.allclose(out, dense, rtol=0, atol=1e-12)
