@@ -28,8 +28,10 @@
 //     = Re[ T_j (Q_g (x + i y)) ],  T_j = e^{i j theta_i},  Q_g = conj(q'_i) e^{i gG theta_i},
 // so per (group, pair) six constants fold dequantization and the group
 // rotation, and per token the lane spends 4 FMAs on Q_g (x + i y) and 2 on
-// the per-token twiddle T_j, staged once per block in LDS.  The 32
-// per-pair partial scores are summed across lanes through LDS.
+// the per-token twiddle T_j, staged once per block in LDS.  The per-pair
+// partial scores of a token are summed across lanes through LDS, or, with
+// one query head, head_dim 128 and 2-bit keys, by DPP row rotations read by
+// the twiddle FMAs themselves and two cross-row swaps (see row_dpp_scores).
 //
 // Code unpacking.  A B-bit field masked in place inside a 16-bit half of a
 // code word, with its lowest bit at position e <= 9, is the binary16 bit
@@ -182,6 +184,39 @@ __device__ __forceinline__ float dpp_all(float v)
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 
+// acc0 += x0(lane q - D) * t0 + y0(lane q - D) * u0 and the same for acc1,
+// where x(lane q - D) is x in lane (q - D) mod 16 of the same 16-lane row
+// (DPP row rotation, read by the FMA itself).  The s_nop gives the two wait
+// states a DPP read needs after the VALU write of its source.
+template <int D>
+__device__ __forceinline__ void fmac_row_ror(float& acc0, float& acc1, float x0, float y0,
+                                             float x1, float y1, float4 t)
+{
+    static_assert(D >= 1 && D <= 15, "row rotation");
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 row_ror:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %3, %7 row_ror:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %4, %8 row_ror:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_ror:%10 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc0), "+v"(acc1)
+        : "v"(x0), "v"(y0), "v"(x1), "v"(y1), "v"(t.x), "v"(t.y), "v"(t.z), "v"(t.w), "i"(D));
+}
+
+// Partial-score terms of two word positions (f and f + 8).
+struct Quad {
+    float4 lo, hi;
+};
+
+// f(std::integral_constant<int, k>) for k = B .. E-1, in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void for_each_int(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        for_each_int<B + 1, E>(f);
+    }
+}
+
 // max(a, b) for operands that are never NaN: a compare and a select, where
 // fmaxf would first quiet both operands.
 __device__ __forceinline__ float max_nn(float a, float b) { return a > b ? a : b; }
@@ -273,7 +308,11 @@ struct Shape {
     static constexpr int NVW = PAIRS ? 2 * WV : QUADS ? 4 * NW : VTOK;  // value code words per lane per step
     static constexpr int NVM = PAIRS ? 2 : QUADS ? 4 : VTOK;            // value meta words per lane per step
     static constexpr int NCL = PAIRS ? G : QUADS ? NW * NC : NC;        // value channels per lane
-    static constexpr int NRED = (QPK == 2 || QPK == 4) ? 2 : 1;  // reduce buffers per wave (heads alternate)
+    // One query head, head_dim 128, 2-bit keys: a token's 64 partial scores
+    // are summed on the VALU (DPP row rotations fused into the twiddle FMAs,
+    // then two cross-row swaps) instead of through LDS; no reduce buffers.
+    static constexpr bool ROWDPP = PAIRS && KB == 2;
+    static constexpr int NRED = ROWDPP ? 0 : (QPK == 2 || QPK == 4) ? 2 : 1;  // reduce buffers per wave (heads alternate)
 };
 
 // Everything one wave step reads from memory, loaded one step ahead.
@@ -779,14 +818,29 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     // once per block: entry (j/2, pair) holds tokens j and j+1 as
     // (T.x, -T.y) pairs.  A separate array from the reduce buffers, so its
     // reads are never ordered after their writes.
+    // With the row-DPP sums (S::ROWDPP) the table is laid out for them
+    // instead: entry (d, pair i), d = 0..15, holds for lane q = i % 16 of row
+    // i / 16 the twiddles of the pair i' = row lane (q - d) mod 16 that the
+    // DPP rotation by d brings in, for token q (.x, .y) and token 16 + q
+    // (.z, .w), scaled by 2^(24 - pos) of word position d, where that pair's
+    // lane keeps those tokens after its rotation by i' % 16 tokens.
     __shared__ float4 twl[G / 2 * 64];
     for (int idx = threadIdx.x; idx < G / 2 * NP; idx += blockDim.x) {
-        const int jp = idx / NP, ii = idx % NP;
-        const float2 t0 = p.rope_offset[(2 * jp) * NP + ii];
-        const float2 t1 = p.rope_offset[(2 * jp + 1) * NP + ii];
-        const float sc0 = (float)(1 << (24 - KC::pos((2 * jp) % KC::TPH)));
-        const float sc1 = (float)(1 << (24 - KC::pos((2 * jp + 1) % KC::TPH)));
-        twl[idx] = make_float4(t0.x * sc0, -t0.y * sc0, t1.x * sc1, -t1.y * sc1);
+        if constexpr (S::ROWDPP) {
+            const int d = idx / NP, ii = idx % NP, qq = ii & 15;
+            const int ip = (ii & ~15) | ((qq - d) & 15);
+            const float sc = (float)(1 << (24 - KC::pos(d % KC::TPH)));
+            const float2 t0 = p.rope_offset[qq * NP + ip];
+            const float2 t1 = p.rope_offset[(16 + qq) * NP + ip];
+            twl[idx] = make_float4(t0.x * sc, -t0.y * sc, t1.x * sc, -t1.y * sc);
+        } else {
+            const int jp = idx / NP, ii = idx % NP;
+            const float2 t0 = p.rope_offset[(2 * jp) * NP + ii];
+            const float2 t1 = p.rope_offset[(2 * jp + 1) * NP + ii];
+            const float sc0 = (float)(1 << (24 - KC::pos((2 * jp) % KC::TPH)));
+            const float sc1 = (float)(1 << (24 - KC::pos((2 * jp + 1) % KC::TPH)));
+            twl[idx] = make_float4(t0.x * sc0, -t0.y * sc0, t1.x * sc1, -t1.y * sc1);
+        }
     }
     // Groups after each wave's first one are taken from a block counter as
     // waves become ready (LDS atomic by one lane), so a wave that also
@@ -803,6 +857,43 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     auto twiddle = [&](int j) {
         const float4 t = twl[(j >> 1) * NP + tw_base];
         return (j & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
+    };
+    // Row-DPP sums: the two tokens of lane q (q and 16 + q) over the 64
+    // pairs.  Every lane of row r holds, in register d of each of its two
+    // key words (after rotating each word by q tokens), token d + q mod 16
+    // of that word; term(d, w) is the twiddled partial score (x, y) of that
+    // register for word w = 0, 1.  Register d of the lane q - d then holds
+    // token q of the word: the DPP rotation by d brings it in, so each lane
+    // sums its tokens over the 16 pairs of its row, and two cross-row swaps
+    // finish the sums.  Returns the score of token lane % 32 (the layout of
+    // the LDS sums).
+    // term(f) gives (x0, y0, x1, y1) of positions f and f + 8 (one code
+    // field of both halves of each word).
+    auto row_dpp_scores = [&](auto&& term) __attribute__((always_inline)) {
+        float acc0, acc1;
+        {
+            const float4 t = twl[tw_base];  // own pair, word position 0
+            const Quad v = term(0);
+            acc0 = fmaf(t.x, v.lo.x, t.y * v.lo.y);
+            acc1 = fmaf(t.z, v.lo.z, t.w * v.lo.w);
+            fmac_row_ror<8>(acc0, acc1, v.hi.x, v.hi.y, v.hi.z, v.hi.w, twl[8 * NP + tw_base]);
+        }
+        for_each_int<1, 8>([&](auto ff) __attribute__((always_inline)) {
+            constexpr int f = decltype(ff)::value;
+            const Quad v = term(f);
+            fmac_row_ror<f>(acc0, acc1, v.lo.x, v.lo.y, v.lo.z, v.lo.w, twl[f * NP + tw_base]);
+            fmac_row_ror<f + 8>(acc0, acc1, v.hi.x, v.hi.y, v.hi.z, v.hi.w,
+                                twl[(f + 8) * NP + tw_base]);
+        });
+        auto rows = [](float v) {
+            const Pair r = swap16(v);
+            v = r.a + r.b;
+            const Pair t = swap32(v);
+            return t.a + t.b;
+        };
+        acc0 = rows(acc0);
+        acc1 = rows(acc1);
+        return (lane & 16) ? acc1 : acc0;
     };
 
     WaveState<QPK, S::NCL> st;
@@ -883,7 +974,45 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         const float s0 = h2f(use.km.x), z0 = h2f(use.km.x >> 16);
         const float s1 = h2f(use.km.y), z1 = h2f(use.km.y >> 16);
         float s[QPK];
-        if constexpr (QPK == 1) {
+        if constexpr (S::ROWDPP) {
+            const float2 Q = cmul(qc[0], use.rg);
+            // X + iY = Q (x + iy): X = P + a c0 + bb c1, Y = R + d c0 + e c1
+            const float P = Q.x * z0 - Q.y * z1, a = Q.x * s0, bb = -Q.y * s1;
+            const float R = Q.y * z0 + Q.x * z1, dq = Q.y * s0, e = Q.x * s1;
+            float Ps[KC::NSCALE], Rs[KC::NSCALE];
+#pragma unroll
+            for (int k = 0; k < KC::NSCALE; ++k) {
+                const float sc = 1.0f / (float)(1 << (24 - k * KB));
+                Ps[k] = P * sc;
+                Rs[k] = R * sc;
+            }
+            // rotate each word right by q tokens (2q bits): register d of
+            // word w then holds token 16 w + (d + q) mod 16
+            const uint32_t rot = 2u * (uint32_t)(lane & 15);
+            uint32_t wx[2], wy[2], wxs[2], wys[2];
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                wx[w] = __builtin_amdgcn_alignbit(use.kw[w], use.kw[w], rot);
+                wy[w] = __builtin_amdgcn_alignbit(use.kw[2 + w], use.kw[2 + w], rot);
+                wxs[w] = wx[w] >> KC::SHIFT;
+                wys[w] = wy[w] >> KC::SHIFT;
+            }
+            s[0] = row_dpp_scores([&](int f) __attribute__((always_inline)) {
+                const int sidx = KC::pos(f) / KB;
+                uint32_t m[4] = {KC::field(wx[0], wxs[0], f), KC::field(wy[0], wys[0], f),
+                                 KC::field(wx[1], wxs[1], f), KC::field(wy[1], wys[1], f)};
+                // one AND per word for both halves (kept whole, not narrowed
+                // per half)
+                asm("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]));
+                auto xy = [&](float c0, float c1) {
+                    return make_float2(fmaf(bb, c1, fmaf(a, c0, Ps[sidx])),
+                                       fmaf(e, c1, fmaf(dq, c0, Rs[sidx])));
+                };
+                const float2 l0 = xy(lo_h(m[0]), lo_h(m[1])), l1 = xy(lo_h(m[2]), lo_h(m[3]));
+                const float2 h0 = xy(hi_h(m[0]), hi_h(m[1])), h1 = xy(hi_h(m[2]), hi_h(m[3]));
+                return Quad{make_float4(l0.x, l0.y, l1.x, l1.y), make_float4(h0.x, h0.y, h1.x, h1.y)};
+            });
+        } else if constexpr (QPK == 1) {
 #pragma unroll
             for (int h = 0; h < QPK; ++h) {
                 const float2 Q = cmul(qc[h], use.rg);
@@ -1102,30 +1231,79 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
             const int cnt = min(G, (in_sink ? ns : n) - t0);
             const size_t row0 = in_sink ? bh * (size_t)p.sink + t0 : bh * (size_t)p.ring + t0 % p.ring;
             const void* const krows = in_sink ? p.k_sink : p.k_tail;
+            // row-DPP sums: register j holds token tok(j), the rotated order
+            // of the group step (lane_q opaque: its 32 row offsets are made
+            // here, not hoisted out of the chunk loop into held registers)
+            int lane_q = lane & 15;
+            asm volatile("" : "+v"(lane_q));
+            auto tok = [&](int j) { return (j & 16) | ((j + lane_q) & 15); };
+            const float2 rg = p.rope_group[(size_t)(t0 / G) * NP + i];
+            float s[QPK];
+            if constexpr (S::ROWDPP) {
+                // registers in the rotated order of the group step; binary16
+                // words kept whole and converted where they are used
+                const float2 Q = cmul(qc[0], rg);
+                auto v4 = [&](float x0, float y0, float x1, float y1, int d) {
+                    // Q (x + iy) at the field scale 2^(pos-24) of the
+                    // register's word position, which the twiddles undo
+                    const float un = 1.0f / (float)(1 << (24 - KC::pos(d % KC::TPH)));
+                    return make_float4((Q.x * x0 - Q.y * y0) * un, (Q.x * y0 + Q.y * x0) * un,
+                                       (Q.x * x1 - Q.y * y1) * un, (Q.x * y1 + Q.y * x1) * un);
+                };
+                if (p.dtype == 0) {
+                    const uint32_t* t32 = reinterpret_cast<const uint32_t*>(krows) + row0 * (D / 2);
+                    uint32_t kr[G];
+#pragma unroll
+                    for (int j = 0; j < G; ++j) {
+                        const int t = tok(j);
+                        kr[j] = t < cnt ? t32[(unsigned)(t * (D / 2) + i)] : 0u;
+                    }
+                    auto at = [&](int d) {
+                        return v4(lo_h(kr[d]), hi_h(kr[d]), lo_h(kr[16 + d]), hi_h(kr[16 + d]), d);
+                    };
+                    s[0] = row_dpp_scores([&](int f) __attribute__((always_inline)) {
+                        return Quad{at(f), at(f + 8)};
+                    });
+                } else {
+                    const float2* t64 = reinterpret_cast<const float2*>(krows) + row0 * (D / 2);
+                    float2 kr[G];
+#pragma unroll
+                    for (int j = 0; j < G; ++j) {
+                        const int t = tok(j);
+                        kr[j] = t < cnt ? t64[(unsigned)(t * (D / 2) + i)] : make_float2(0.f, 0.f);
+                    }
+                    auto at = [&](int d) {
+                        return v4(kr[d].x, kr[d].y, kr[16 + d].x, kr[16 + d].y, d);
+                    };
+                    s[0] = row_dpp_scores([&](int f) __attribute__((always_inline)) {
+                        return Quad{at(f), at(f + 8)};
+                    });
+                }
+            }
             float tx[G], ty[G];
-            const size_t trow = row0 * D + 2 * i;  // element index of (token t0, channel 2i)
-            if (p.dtype == 0) {
-                const uint32_t* t32 = reinterpret_cast<const uint32_t*>(krows) + trow / 2;
+            if (S::ROWDPP) {
+            } else if (p.dtype == 0) {
+                // rows of D binary16: a uniform base and a 32-bit lane offset
+                const uint32_t* t32 = reinterpret_cast<const uint32_t*>(krows) + row0 * (D / 2);
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
-                    const uint32_t w = (gsub == 0 && j < cnt) ? t32[(size_t)j * (D / 2)] : 0u;
+                    const uint32_t w =
+                        (gsub == 0 && j < cnt) ? t32[(unsigned)(j * (D / 2) + i)] : 0u;
                     tx[j] = lo_h(w);
                     ty[j] = hi_h(w);
                 }
             } else {
-                const float2* t64 = reinterpret_cast<const float2*>(krows) + trow / 2;
+                const float2* t64 = reinterpret_cast<const float2*>(krows) + row0 * (D / 2);
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
-                    const float2 w = (gsub == 0 && j < cnt) ? t64[(size_t)j * (D / 2)]
+                    const float2 w = (gsub == 0 && j < cnt) ? t64[(unsigned)(j * (D / 2) + i)]
                                                             : make_float2(0.f, 0.f);
                     tx[j] = w.x;
                     ty[j] = w.y;
                 }
             }
-            const float2 rg = p.rope_group[(size_t)(t0 / G) * NP + i];
-            float s[QPK];
 #pragma unroll
-            for (int h = 0; h < QPK; ++h) {
+            for (int h = 0; h < (S::ROWDPP ? 0 : QPK); ++h) {
                 const float2 Q = cmul(qc[h], rg);
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
