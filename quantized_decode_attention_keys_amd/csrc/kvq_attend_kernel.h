@@ -202,9 +202,11 @@ __device__ __forceinline__ void fmac_row_ror(float& acc0, float& acc1, float x0,
         : "v"(x0), "v"(y0), "v"(x1), "v"(y1), "v"(t.x), "v"(t.y), "v"(t.z), "v"(t.w), "i"(D));
 }
 
-// Partial-score terms of two word positions (f and f + 8).
-struct Quad {
-    float4 lo, hi;
+// Partial-score terms (x0, y0, x1, y1) of N positions of the two 16-token
+// units of a lane's key words.
+template <int N>
+struct Terms {
+    float4 v[N];
 };
 
 // f(std::integral_constant<int, k>) for k = B .. E-1, in order.
@@ -308,10 +310,14 @@ struct Shape {
     static constexpr int NVW = PAIRS ? 2 * WV : QUADS ? 4 * NW : VTOK;  // value code words per lane per step
     static constexpr int NVM = PAIRS ? 2 : QUADS ? 4 : VTOK;            // value meta words per lane per step
     static constexpr int NCL = PAIRS ? G : QUADS ? NW * NC : NC;        // value channels per lane
-    // One query head, head_dim 128, 2-bit keys: a token's 64 partial scores
-    // are summed on the VALU (DPP row rotations fused into the twiddle FMAs,
-    // then two cross-row swaps) instead of through LDS; no reduce buffers.
-    static constexpr bool ROWDPP = PAIRS && KB == 2;
+    // One query head, head_dim 128, 2-bit keys (or 4-bit keys with 2-bit
+    // values): a token's 64 partial scores are summed on the VALU (DPP row
+    // rotations fused into the twiddle FMAs, then two cross-row swaps)
+    // instead of through LDS; no reduce buffers.  (With 4-bit keys and
+    // 4-bit values the rotations cost most of the saving and the main loop
+    // spilled registers.)
+    static constexpr bool ROWDPP = PAIRS && (KB == 2 || (KB == 4 && VB == 2));
+    static constexpr int WPU = KB / 2;          // row-DPP: key words per 16-token unit
     static constexpr int NRED = ROWDPP ? 0 : (QPK == 2 || QPK == 4) ? 2 : 1;  // reduce buffers per wave (heads alternate)
 };
 
@@ -859,31 +865,32 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         return (j & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
     };
     // Row-DPP sums: the two tokens of lane q (q and 16 + q) over the 64
-    // pairs.  Every lane of row r holds, in register d of each of its two
-    // key words (after rotating each word by q tokens), token d + q mod 16
-    // of that word; term(d, w) is the twiddled partial score (x, y) of that
-    // register for word w = 0, 1.  Register d of the lane q - d then holds
-    // token q of the word: the DPP rotation by d brings it in, so each lane
-    // sums its tokens over the 16 pairs of its row, and two cross-row swaps
-    // finish the sums.  Returns the score of token lane % 32 (the layout of
-    // the LDS sums).
-    // term(f) gives (x0, y0, x1, y1) of positions f and f + 8 (one code
-    // field of both halves of each word).
+    // pairs.  The key words of a channel form two 16-token units (tokens
+    // 0..15 and 16..31; one word each at 2 bits, two at 4).  Every lane
+    // rotates each unit by q tokens, so its position d (0..15) holds token
+    // d + q mod 16 of the unit; then position d of the lane q - d of the
+    // same row holds token q of the unit, and a DPP rotation by d brings it
+    // in.  Each lane sums its two tokens over the 16 pairs of its row, and
+    // two cross-row swaps finish the sums.  term(f) gives the twiddled
+    // partial scores (x0, y0, x1, y1) of positions p * TPH + f, p < NPOS
+    // (one code field f of each half-word of a unit).  Returns the score of
+    // token lane % 32 (the layout of the LDS sums).
+    constexpr int NPOS = 2 * S::WPU;
     auto row_dpp_scores = [&](auto&& term) __attribute__((always_inline)) {
-        float acc0, acc1;
-        {
-            const float4 t = twl[tw_base];  // own pair, word position 0
-            const Quad v = term(0);
-            acc0 = fmaf(t.x, v.lo.x, t.y * v.lo.y);
-            acc1 = fmaf(t.z, v.lo.z, t.w * v.lo.w);
-            fmac_row_ror<8>(acc0, acc1, v.hi.x, v.hi.y, v.hi.z, v.hi.w, twl[8 * NP + tw_base]);
-        }
-        for_each_int<1, 8>([&](auto ff) __attribute__((always_inline)) {
+        float acc0 = 0.f, acc1 = 0.f;
+        for_each_int<0, KC::TPH>([&](auto ff) __attribute__((always_inline)) {
             constexpr int f = decltype(ff)::value;
-            const Quad v = term(f);
-            fmac_row_ror<f>(acc0, acc1, v.lo.x, v.lo.y, v.lo.z, v.lo.w, twl[f * NP + tw_base]);
-            fmac_row_ror<f + 8>(acc0, acc1, v.hi.x, v.hi.y, v.hi.z, v.hi.w,
-                                twl[(f + 8) * NP + tw_base]);
+            const Terms<NPOS> v = term(f);
+            for_each_int<0, NPOS>([&](auto pp) __attribute__((always_inline)) {
+                constexpr int pi = decltype(pp)::value, d = pi * KC::TPH + f;
+                const float4 t = twl[d * NP + tw_base];
+                if constexpr (d == 0) {  // the lane's own pair
+                    acc0 = fmaf(t.x, v.v[pi].x, t.y * v.v[pi].y);
+                    acc1 = fmaf(t.z, v.v[pi].z, t.w * v.v[pi].w);
+                } else {
+                    fmac_row_ror<d>(acc0, acc1, v.v[pi].x, v.v[pi].y, v.v[pi].z, v.v[pi].w, t);
+                }
+            });
         });
         auto rows = [](float v) {
             const Pair r = swap16(v);
@@ -986,31 +993,56 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                 Ps[k] = P * sc;
                 Rs[k] = R * sc;
             }
-            // rotate each word right by q tokens (2q bits): register d of
-            // word w then holds token 16 w + (d + q) mod 16
-            const uint32_t rot = 2u * (uint32_t)(lane & 15);
-            uint32_t wx[2], wy[2], wxs[2], wys[2];
+            // rotate each 16-token unit right by q tokens (KB * q bits):
+            // position d of unit u then holds token 16 u + (d + q) mod 16
+            constexpr int WPU = S::WPU;
+            const uint32_t q16 = (uint32_t)(lane & 15);
+            uint32_t wr[2][2][WPU];  // [channel x, y][unit][word]
 #pragma unroll
-            for (int w = 0; w < 2; ++w) {
-                wx[w] = __builtin_amdgcn_alignbit(use.kw[w], use.kw[w], rot);
-                wy[w] = __builtin_amdgcn_alignbit(use.kw[2 + w], use.kw[2 + w], rot);
-                wxs[w] = wx[w] >> KC::SHIFT;
-                wys[w] = wy[w] >> KC::SHIFT;
-            }
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint32_t* w = use.kw + c * S::WK + u * WPU;
+                    if constexpr (WPU == 1) {
+                        wr[c][u][0] = __builtin_amdgcn_alignbit(w[0], w[0], 2u * q16);
+                    } else {
+                        const uint64_t x = ((uint64_t)w[1] << 32) | w[0];
+                        const uint32_t sh = (uint32_t)KB * q16;  // < 64
+                        const uint64_t r = (x >> sh) | (x << ((64u - sh) & 63u));
+                        wr[c][u][0] = (uint32_t)r;
+                        wr[c][u][1] = (uint32_t)(r >> 32);
+                    }
+                }
             s[0] = row_dpp_scores([&](int f) __attribute__((always_inline)) {
                 const int sidx = KC::pos(f) / KB;
-                uint32_t m[4] = {KC::field(wx[0], wxs[0], f), KC::field(wy[0], wys[0], f),
-                                 KC::field(wx[1], wxs[1], f), KC::field(wy[1], wys[1], f)};
-                // one AND per word for both halves (kept whole, not narrowed
-                // per half)
-                asm("" : "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]));
+                // field f of each word, both halves from one AND (kept
+                // whole, not narrowed per half)
+                uint32_t m[2][2][WPU];
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int k = 0; k < WPU; ++k) {
+                            const uint32_t w = wr[c][u][k];
+                            m[c][u][k] = KC::field(w, w >> KC::SHIFT, f);
+                            asm("" : "+v"(m[c][u][k]));
+                        }
                 auto xy = [&](float c0, float c1) {
                     return make_float2(fmaf(bb, c1, fmaf(a, c0, Ps[sidx])),
                                        fmaf(e, c1, fmaf(dq, c0, Rs[sidx])));
                 };
-                const float2 l0 = xy(lo_h(m[0]), lo_h(m[1])), l1 = xy(lo_h(m[2]), lo_h(m[3]));
-                const float2 h0 = xy(hi_h(m[0]), hi_h(m[1])), h1 = xy(hi_h(m[2]), hi_h(m[3]));
-                return Quad{make_float4(l0.x, l0.y, l1.x, l1.y), make_float4(h0.x, h0.y, h1.x, h1.y)};
+                Terms<NPOS> v;
+#pragma unroll
+                for (int k = 0; k < WPU; ++k)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        auto half = [&](uint32_t x) { return h ? hi_h(x) : lo_h(x); };
+                        const float2 t0 = xy(half(m[0][0][k]), half(m[1][0][k]));
+                        const float2 t1 = xy(half(m[0][1][k]), half(m[1][1][k]));
+                        v.v[2 * k + h] = make_float4(t0.x, t0.y, t1.x, t1.y);
+                    }
+                return v;
             });
         } else if constexpr (QPK == 1) {
 #pragma unroll
@@ -1262,7 +1294,11 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                         return v4(lo_h(kr[d]), hi_h(kr[d]), lo_h(kr[16 + d]), hi_h(kr[16 + d]), d);
                     };
                     s[0] = row_dpp_scores([&](int f) __attribute__((always_inline)) {
-                        return Quad{at(f), at(f + 8)};
+                        Terms<NPOS> v;
+#pragma unroll
+                        for (int pi = 0; pi < NPOS; ++pi)
+                            v.v[pi] = at(pi * KC::TPH + f);
+                        return v;
                     });
                 } else {
                     const float2* t64 = reinterpret_cast<const float2*>(krows) + row0 * (D / 2);
@@ -1276,7 +1312,11 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
                         return v4(kr[d].x, kr[d].y, kr[16 + d].x, kr[16 + d].y, d);
                     };
                     s[0] = row_dpp_scores([&](int f) __attribute__((always_inline)) {
-                        return Quad{at(f), at(f + 8)};
+                        Terms<NPOS> v;
+#pragma unroll
+                        for (int pi = 0; pi < NPOS; ++pi)
+                            v.v[pi] = at(pi * KC::TPH + f);
+                        return v;
                     });
                 }
             }
