@@ -1399,8 +1399,13 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
 
     __builtin_amdgcn_s_setprio(0);
 
-    // ---- merge the waves of this block
-    __syncthreads();  // every wave is done with its reduce buffer
+    // ---- merge the waves of this block.  The merge area overlaps the
+    // reduce buffers, so every wave must be done with its own first; the
+    // row-DPP variants have none (nothing but the twiddles is in LDS during
+    // their loop), so a wave that finishes early reduces and stores its
+    // state at once, while the others still run.
+    if constexpr (!S::ROWDPP)
+        __syncthreads();
     float* sm = smem;                           // [nwaves][QPK]
     float* sl = smem + kMaxWaves * QPK;         // [nwaves][QPK]
     float* so = smem + 2 * kMaxWaves * QPK;     // [nwaves][QPK][D]
@@ -1498,14 +1503,37 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     for (int idx = tid; idx < QPK * D; idx += blockDim.x) {
         const int h = idx / D, c = idx % D;
         float M = -INFINITY;
-        for (int w = 0; w < nwaves; ++w)
-            M = fmaxf(M, sm[w * QPK + h]);
         float L = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-            for (int w = 0; w < nwaves; ++w) {
-                const float f = exp2f(sm[w * QPK + h] - M);
-                L += f * sl[w * QPK + h];
-                acc += f * so[(w * QPK + h) * D + c];
+        if constexpr (S::ROWDPP) {
+            // unrolled to the largest block, waves past nwaves reading wave
+            // 0's slots and weighing nothing, so all the reads issue at once
+            constexpr int kW = max_block_waves(QPK);
+            float mw[kW], lw[kW], ow[kW];
+#pragma unroll
+            for (int w = 0; w < kW; ++w) {
+                const int ww = w < nwaves ? w : 0;
+                mw[w] = w < nwaves ? sm[ww * QPK + h] : -INFINITY;
+                lw[w] = sl[ww * QPK + h];
+                ow[w] = so[(ww * QPK + h) * D + c];
+                M = fmaxf(M, mw[w]);
+            }
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < kW; ++w) {
+                    const float f = exp2f(mw[w] - M);
+                    L += f * lw[w];
+                    acc += f * ow[w];
+                }
+            }
+        } else {
+            for (int w = 0; w < nwaves; ++w)
+                M = fmaxf(M, sm[w * QPK + h]);
+            if (M != -INFINITY) {
+                for (int w = 0; w < nwaves; ++w) {
+                    const float f = exp2f(sm[w * QPK + h] - M);
+                    L += f * sl[w * QPK + h];
+                    acc += f * so[(w * QPK + h) * D + c];
+                }
             }
         }
         const size_t row = (size_t)b * p.hq + head0 + h;
