@@ -38,6 +38,23 @@ def test_prefill_d128(S, R, n, qpk):
     _check(cfg, cache, k, v, n, R, S, cap)
 
 
+@pytest.mark.parametrize("bits", [(2, 2), (4, 2)])
+@pytest.mark.parametrize("dtype", ["float16", "float32"])
+def test_prefill_d128_one_head_windows(bits, dtype):
+    """One query head per KV head at head_dim 128 with 2-bit keys, or 4-bit
+    keys and 2-bit values (the variants whose scores are summed by DPP row
+    rotations): sink and window chunks loaded in the rotated token order,
+    binary16 and fp32 rows."""
+    cfg = synth.scaled(synth.CONFIGS["llama2_7b"], batch=2, kv_heads=2, q_heads=2, n_tokens=300,
+                       key_bits=bits[0], value_bits=bits[1], dtype=dtype)
+    n, S, R, cap = 300, 32, 64, 320
+    k = synth.make_keys(cfg, 0, 0, n)
+    v = synth.make_values(cfg, 0, 0, n)
+    cache = make_cache(cfg, cap, residual=R, sink=S)
+    cache.prefill(to_gpu(k), to_gpu(v))
+    _check(cfg, cache, k, v, n, R, S, cap)
+
+
 @pytest.mark.parametrize("dtype", ["float16", "float32"])
 def test_prefill_d64(dtype):
     cfg = synth.scaled(synth.CONFIGS["tiny"], kv_heads=2, q_heads=4, key_bits=4, value_bits=2,
