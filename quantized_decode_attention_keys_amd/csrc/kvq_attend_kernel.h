@@ -871,10 +871,12 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
     // d + q mod 16 of the unit; then position d of the lane q - d of the
     // same row holds token q of the unit, and a DPP rotation by d brings it
     // in.  Each lane sums its two tokens over the 16 pairs of its row, and
-    // two cross-row swaps finish the sums.  term(f) gives the twiddled
-    // partial scores (x0, y0, x1, y1) of positions p * TPH + f, p < NPOS
-    // (one code field f of each half-word of a unit).  Returns the score of
-    // token lane % 32 (the layout of the LDS sums).
+    // two cross-row swaps finish the sums.  term(f) gives, for positions
+    // p * TPH + f, p < NPOS (code field f of each half-word of a unit), the
+    // (X, Y) = Q (x + iy) of unit 0 and of unit 1 at the field scale of that
+    // position; the twiddle table (T.x, -T.y) * 2^(24 - pos) turns them into
+    // partial scores.  Returns the score of token lane % 32 (the layout of
+    // the LDS sums).
     constexpr int NPOS = 2 * S::WPU;
     auto row_dpp_scores = [&](auto&& term) __attribute__((always_inline)) {
         float acc0 = 0.f, acc1 = 0.f;
@@ -983,7 +985,7 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
         float s[QPK];
         if constexpr (S::ROWDPP) {
             const float2 Q = cmul(qc[0], use.rg);
-            // X + iY = Q (x + iy): X = P + a c0 + bb c1, Y = R + d c0 + e c1
+            // X + iY = Q (x + iy): X = P + a c0 + bb c1, Y = R + dq c0 + e c1
             const float P = Q.x * z0 - Q.y * z1, a = Q.x * s0, bb = -Q.y * s1;
             const float R = Q.y * z0 + Q.x * z1, dq = Q.y * s0, e = Q.x * s1;
             float Ps[KC::NSCALE], Rs[KC::NSCALE];
