@@ -398,7 +398,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU component in this build)", file=sys.stderr)
+              "(the library has no multi-GPU component)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
