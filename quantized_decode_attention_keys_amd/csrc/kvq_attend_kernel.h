@@ -316,7 +316,8 @@ struct Shape {
     // instead of through LDS; no reduce buffers.  (With 4-bit keys and
     // 4-bit values the rotations cost most of the saving and the main loop
     // spilled registers.)
-    static constexpr bool ROWDPP = PAIRS && (KB == 2 || (KB == 4 && VB == 2));
+    static constexpr bool ROWDPP = row_dpp_sums(D, KB, VB, QPK);
+    static_assert(!ROWDPP || PAIRS, "row-DPP sums use the one-head value layout");
     static constexpr int WPU = KB / 2;          // row-DPP: key words per 16-token unit
     static constexpr int NRED = ROWDPP ? 0 : (QPK == 2 || QPK == 4) ? 2 : 1;  // reduce buffers per wave (heads alternate)
 };

@@ -151,12 +151,16 @@ int settle(const kvq* h, void* stream, int st)
     return hip_status(e);
 }
 
-// Launch shape of the decode-attention kernel.  A compute unit holds about
-// 12 waves of the one-query-head kernel (8 when several query heads share a
+// Launch shape of the decode-attention kernel.  A compute unit holds 16
+// waves of the one-query-head kernel (8 when several query heads share a
 // KV head: more registers).  Best measured: blocks of that full size, with
 // splits chosen so that blocks = k * CUs for a small k (every CU gets the
-// same whole number of blocks); without such a fit, 4-wave blocks and enough
-// splits for about three blocks per CU, which keeps the last round short.
+// same whole number of blocks).  Without such a fit: 8-wave blocks and at
+// least two splits for the variants with row-DPP sums (no LDS reduce
+// buffers; 13B shape 148-149 us against 151-153 us with 4-wave blocks);
+// otherwise 4-wave blocks and enough splits for about three blocks per CU,
+// which keeps the last round short (their reduce buffers limit larger
+// blocks to one per CU: 211-215 us against 180-183 us at 4-bit values).
 void attend_shape(const kvq* h, int n, int* splits_out, int* waves_out)
 {
     const int qpk_all = h->cfg.q_heads / h->cfg.kv_heads;
@@ -181,8 +185,12 @@ void attend_shape(const kvq* h, int n, int* splits_out, int* waves_out)
         }
     }
     if (splits == 0) {
-        waves = 4;
+        const bool rowdpp = kvqi::row_dpp_sums(h->cfg.head_dim, h->cfg.key_bits,
+                                               h->cfg.value_bits, kvqi::block_heads(qpk_all));
+        waves = rowdpp ? 8 : 4;
         splits = (int)(((long long)(wpc / waves) * cus + units - 1) / units);
+        if (rowdpp && splits < 2)
+            splits = 2;
         if (splits > max_splits)
             splits = max_splits;
         if (splits < 1)

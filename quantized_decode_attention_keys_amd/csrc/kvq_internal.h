@@ -20,6 +20,15 @@ constexpr int max_block_waves(int qpk) { return qpk == 1 ? 16 : 8; }
 // as two blocks of 4 over the same KV head.
 constexpr int block_heads(int qpk) { return qpk < 4 ? qpk : 4; }
 
+// Attention variants whose per-pair partial scores are summed by DPP row
+// rotations instead of through LDS (one query head per block, head_dim 128,
+// 2-bit keys or 4-bit keys with 2-bit values): they need no LDS reduce
+// buffers.
+constexpr bool row_dpp_sums(int head_dim, int kbits, int vbits, int block_qpk)
+{
+    return block_qpk == 1 && head_dim == 128 && (kbits == 2 || (kbits == 4 && vbits == 2));
+}
+
 // Everything a kernel needs to address the planes of one cache.
 struct Planes {
     uint32_t* k_codes;   // [nb][hkv][gcap][D][wk]
