@@ -185,8 +185,10 @@ void attend_shape(const kvq* h, int n, int* splits_out, int* waves_out)
         }
     }
     if (splits == 0) {
+        // (the 8-wave rule where it was measured: fewer units than 4 per CU)
         const bool rowdpp = kvqi::row_dpp_sums(h->cfg.head_dim, h->cfg.key_bits,
-                                               h->cfg.value_bits, kvqi::block_heads(qpk_all));
+                                               h->cfg.value_bits, kvqi::block_heads(qpk_all)) &&
+                            units < 4 * cus;
         waves = rowdpp ? 8 : 4;
         splits = (int)(((long long)(wpc / waves) * cus + units - 1) / units);
         if (rowdpp && splits < 2)
