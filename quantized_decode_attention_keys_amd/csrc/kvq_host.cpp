@@ -157,7 +157,8 @@ int settle(const kvq* h, void* stream, int st)
 // splits chosen so that blocks = k * CUs for a small k (every CU gets the
 // same whole number of blocks).  Without such a fit: 8-wave blocks and at
 // least two splits for the variants with row-DPP sums (no LDS reduce
-// buffers; 13B shape 148-149 us against 151-153 us with 4-wave blocks);
+// buffers) when there are fewer than 4 units per CU (13B shape 147-150 us
+// against 151-153 us with 4-wave blocks; larger counts were not measured);
 // otherwise 4-wave blocks and enough splits for about three blocks per CU,
 // which keeps the last round short (their reduce buffers limit larger
 // blocks to one per CU: 211-215 us against 180-183 us at 4-bit values).
