@@ -1555,26 +1555,50 @@ __global__ __launch_bounds__(64 * max_block_waves(QPK)) void attend_kernel(Plane
 
 // Merge the split partials of one output row (grid: batch * q_heads rows,
 // head_dim threads): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// A split whose m is -inf saw no tokens and is skipped.
+// Splits go in chunks of kChunk whose loads all issue before any is used
+// (a slot past the last split reads the chunk's first split again with
+// m = -inf), merged online.  A split whose m is -inf (no tokens; its o and
+// l are stored as 0) or a slot past the end gets the weight 2^-inf = 0
+// exactly, so with at most kChunk splits the sums equal those of the
+// two-pass form that skips such splits.
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ partials,
                                                     int max_splits, int splits,
                                                     float* __restrict__ out)
 {
+    constexpr int kChunk = 8;
     const size_t row = blockIdx.x;
     const int c = threadIdx.x;
     const float* base = partials + row * max_splits * (D + 2);
-    float M = -INFINITY;
-    for (int sp = 0; sp < splits; ++sp)
-        M = fmaxf(M, base[sp * (D + 2) + D]);
-    float L = 0.f, acc = 0.f;
-    for (int sp = 0; sp < splits; ++sp) {
-        const float ms = base[sp * (D + 2) + D];
-        if (ms == -INFINITY)
-            continue;
-        const float f = exp2f(ms - M);
-        L += f * base[sp * (D + 2) + D + 1];
-        acc += f * base[sp * (D + 2) + c];
+    float M = -INFINITY, L = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += kChunk) {
+        float mv[kChunk], lv[kChunk], ov[kChunk];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const bool in = s0 + u < splits;
+            const float* b = base + (size_t)(in ? s0 + u : s0) * (D + 2);
+            mv[u] = in ? b[D] : -INFINITY;
+            lv[u] = b[D + 1];
+            ov[u] = b[c];
+        }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u)
+            Mn = fmaxf(Mn, mv[u]);
+        // reference maximum: 0 while no split so far saw tokens (all weights
+        // 0 then); the earlier chunks' sums rescale by 2^(M - Mn), which is
+        // 0 when M = -inf (the sums are still 0) and 1 when Mn = M
+        const float Mr = Mn == -INFINITY ? 0.f : Mn;
+        const float r = exp2f(M - Mr);
+        L *= r;
+        acc *= r;
+        M = Mn;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const float f = exp2f(mv[u] - Mr);
+            L += f * lv[u];
+            acc += f * ov[u];
+        }
     }
     out[row * D + c] = acc / L;
 }
