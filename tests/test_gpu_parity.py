@@ -83,7 +83,9 @@ def test_scores_monotone_in_position(bits, qpk, direction):
     running maximum and rescales the accumulators) or fall (only the first
     step does).  The keys' energy sits in the last channel, which either
     rotary pairing turns at the lowest frequency (under 0.12 rad over 1000
-    tokens), so q.k follows the key's magnitude there."""
+    tokens), so q.k follows the key's magnitude there.  The shape runs 31
+    token splits, merged in chunks of 8: rising scores put the maximum in
+    the last chunk, so the sums of the earlier chunks are rescaled."""
     cfg = synth.scaled(synth.CONFIGS["llama2_7b"], batch=2, kv_heads=2, q_heads=2 * qpk,
                        n_tokens=1000, key_bits=bits[0], value_bits=bits[1])
     n, D = 1000, cfg.head_dim
