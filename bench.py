@@ -23,6 +23,9 @@ with the VALU view beside it.  A third set of event-timed steps writes a
 1 GiB scratch buffer before each step (flushing the Infinity Cache), so each
 line also shows whether cache residency inflates the rotating-cache figure.
 
+The prefill figure times the caches' prompt prefills enqueued back to back
+(the first, after an idle GPU, reported apart).
+
 --decode-loop K (with --config llama2_13b or llama2_13b_b4): prefill the
 prompt once, then time K consecutive decode steps on that one cache end to
 end (appends included, no flush inside the loop); prints tokens/s = batch *
@@ -449,21 +452,26 @@ def main():
                                cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev,
                                residual=Rw, sink=Sw, geometry=geom, format=int(fp8))
               for _ in range(R)]
-    # prefill (quantize-and-pack of the whole prompt), timed per cache after
-    # one untimed prefill of a one-group cache (first launches load the code)
+    # prefill (quantize-and-pack of the whole prompt) of every cache, after
+    # one untimed prefill of a one-group cache (first launches load the code).
+    # The caches' prefills are enqueued back to back with an event after
+    # each: while one runs the host enqueues the next, so the time between
+    # consecutive events is the GPU's.  The first follows an idle GPU and
+    # also holds the host's enqueue; it is reported apart and, with two or
+    # more caches, left out of the median.
     warm = QuantizedKVCache(cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.group,
                             cfg.key_bits, cfg.value_bits, tdt, cfg.rope_base, device=dev)
     warm.prefill(k[:, :, :cfg.group].contiguous(), v[:, :, :cfg.group].contiguous())
     torch.cuda.synchronize()
     warm.close()
-    pf_ms = []
-    for c in caches:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+    pf_ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(caches) + 1)]
+    pf_ev[0].record()
+    for i, c in enumerate(caches):
         c.prefill(k, v)
-        e1.record()
-        torch.cuda.synchronize()
-        pf_ms.append(e0.elapsed_time(e1))
+        pf_ev[i + 1].record()
+    torch.cuda.synchronize()
+    pf_all = [pf_ev[i].elapsed_time(pf_ev[i + 1]) for i in range(len(caches))]
+    pf_ms = pf_all[1:] if len(pf_all) > 1 else pf_all
     # error where it is consumed, on the first cache's prompt (before the
     # appends): the unquantized prompt keys and values are still at hand
     metrics = None
@@ -659,6 +667,8 @@ def main():
         "prefill": {
             "tokens": n - 1,
             "median_ms": round(float(np.median(pf_ms)), 4),
+            "samples": len(pf_ms),
+            "first_call_ms": round(pf_all[0], 4),
             "GB_per_s": round((3 * fp8_bytes(cfg, n - 1, with_q=False) if fp8 else
                                prefill_bytes(cfg, n - 1, Rw, Sw, geom))
                               / (np.median(pf_ms) / 1e3) / 1e9, 2),
