@@ -128,6 +128,18 @@ def test_eight_heads_per_kv_head_take_the_two_call_path():
     assert worst == 0.0, worst
 
 
+@pytest.mark.parametrize("window", [(0, 0), (32, 0)])
+def test_fills_to_a_ragged_capacity(window):
+    """max_tokens = 77, not a multiple of G: the cache is stepped through
+    the flush at 64 to exactly max_tokens, where the last group (tokens 64
+    .. 76) is still partial and its planes' slots run past the capacity.
+    With a residual window the step takes the two-call path."""
+    residual, sink = window
+    cfg = synth.scaled(L7B, batch=2, kv_heads=2, q_heads=4, n_tokens=77)
+    worst = _run(cfg, 40, 77, 77, residual=residual, sink=sink, checks=(63, 64, 65))
+    assert worst <= (AGREE if residual == 0 else 0.0), worst
+
+
 def test_capacity_error_leaves_state_unchanged():
     from quantized_decode_attention_keys_amd import KVQ_ERR_CAPACITY, KvqError
     cfg = synth.scaled(TINY, n_tokens=33)
